@@ -1,0 +1,73 @@
+"""Plain float64 scaled-dot-product attention (test infrastructure only).
+
+Definition followed (FlashAttention 2 + 3 — speicherbewusste Attention-Kernels, "Kernpunkte": the
+tiled kernel returns exactly what softmax(Q K^T / sqrt(d)) V returns; "Worum es geht": it is not a
+different formula, only a different data movement).  For one (batch, head), query row i and the
+visible key set J(i) = {0..N-1} (non-causal) or {0..i} (causal, lower-triangular):
+
+    s_ij = scale * sum_t Q[i,t] K[j,t]                  for j in J(i)
+    m_i  = max_j s_ij
+    l_i  = sum_j exp(s_ij - m_i)
+    O_i  = sum_j exp(s_ij - m_i) V[j] / l_i
+    lse_i = m_i + ln l_i
+
+Subtracting m_i is the algebraic identity exp(s - m)/sum exp(s - m) = exp(s)/sum exp(s), used only so
+that exp never overflows.  Each query row is computed from its full score row in one step: no
+splitting of the keys into tiles and no running maximum (that is what the GPU kernel does instead).
+All arithmetic is float64 on the exact (already rounded) input values.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    """Exact upcast of a numpy array or CPU torch tensor (any float dtype) to float64."""
+    if hasattr(x, "detach"):
+        x = x.detach().cpu()
+        if str(x.dtype) in ("torch.bfloat16", "torch.float16"):
+            x = x.float()
+        x = x.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def attention_rows(qh, kh, vh, rows, causal: bool, scale: float):
+    """Attention output and lse for selected query rows of ONE head.
+
+    qh: [N, d] queries, kh/vh: [N, d] keys/values, rows: 1-D integer array of query indices.
+    Returns (O [len(rows), d] float64, lse [len(rows)] float64).
+    """
+    qh, kh, vh = _f64(qh), _f64(kh), _f64(vh)
+    rows = np.asarray(rows, dtype=np.int64)
+    n_keys = kh.shape[0]
+    s = float(scale) * (qh[rows] @ kh.T)  # [r, N]
+    if causal:
+        visible = np.arange(n_keys)[None, :] <= rows[:, None]
+        s = np.where(visible, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)  # exp(-inf) = 0 for hidden keys
+    l = e.sum(axis=1, keepdims=True)
+    o = (e @ vh) / l
+    lse = m[:, 0] + np.log(l[:, 0])
+    return o, lse
+
+
+def attention_ref(q, k, v, causal: bool, scale: float, row_chunk: int = 1024):
+    """Full attention for tensors [..., N, d] (leading dims = batch, heads).
+
+    Returns (O float64 [..., N, d], lse float64 [..., N]).  Query rows are processed in chunks of
+    ``row_chunk`` only to bound memory; every chunk sees all of its keys at once.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lead = q.shape[:-2]
+    n, d = q.shape[-2], q.shape[-1]
+    o = np.empty(lead + (n, v.shape[-1]), dtype=np.float64)
+    lse = np.empty(lead + (n,), dtype=np.float64)
+    for idx in np.ndindex(*lead):
+        for r0 in range(0, n, row_chunk):
+            rows = np.arange(r0, min(n, r0 + row_chunk))
+            o_c, lse_c = attention_rows(q[idx], k[idx], v[idx], rows, causal, scale)
+            o[idx][r0:r0 + len(rows)] = o_c
+            lse[idx][r0:r0 + len(rows)] = lse_c
+    return o, lse
