@@ -1,0 +1,19 @@
+"""Exact tiled attention forward for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libfa.so`` (hand-written HIP kernels behind the C ABI of ``include/fa.h``);
+this package only loads it and marshals arguments.
+"""
+
+from .binding import (  # noqa: F401
+    FA_BF16,
+    FA_F16,
+    FA_F32,
+    FA_FP8_E4M3,
+    FaError,
+    abi_version,
+    fp8_prep,
+    fwd,
+    last_error,
+    lib,
+    status_str,
+)

@@ -1,0 +1,163 @@
+"""Python binding of libfa.so (ctypes).  Argument marshalling only: every step of the attention
+forward and the fp8 preparation runs in the library's HIP kernels.  torch supplies device memory
+and the current stream.  There is no fallback: if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2, 3
+DTYPE_CODE = {
+    torch.float32: FA_F32,
+    torch.float16: FA_F16,
+    torch.bfloat16: FA_BF16,
+    torch.float8_e4m3fn: FA_FP8_E4M3,
+}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """Non-FA_OK status from the library; ``status`` holds the code."""
+
+    def __init__(self, status: int, func: str, detail: str):
+        super().__init__(f"{func} -> {status_str(status)} ({detail})")
+        self.status = status
+
+
+class _Fp8Scales(ctypes.Structure):
+    _fields_ = [
+        ("q_scale", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("block", ctypes.c_int),
+    ]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so from this package directory (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(or python -m exact_tiled_attention_22_amd.build_lib)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.fa_fwd.restype = i
+    L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, ctypes.POINTER(_Fp8Scales), vp]
+    L.fa_fwd_ex.restype = i
+    L.fa_fp8_prep.argtypes = [vp, i, vp, vp, vp, i, i, i, i, vp]
+    L.fa_fp8_prep.restype = i
+    L.fa_status_str.argtypes = [i]
+    L.fa_status_str.restype = ctypes.c_char_p
+    L.fa_last_error.argtypes = []
+    L.fa_last_error.restype = ctypes.c_char_p
+    L.fa_abi_version.argtypes = []
+    L.fa_abi_version.restype = i
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().fa_status_str(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().fa_last_error().decode()
+
+
+def abi_version() -> int:
+    return int(lib().fa_abi_version())
+
+
+def _check(status: int, func: str) -> None:
+    if status != 0:
+        raise FaError(status, func, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_qkv(q, k, v):
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in DTYPE_CODE:
+        raise ValueError(f"unsupported or mixed dtypes {q.dtype}, {k.dtype}, {v.dtype}")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous [B, H, N, d]")
+
+
+def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
+        return_lse: bool = True, fp8_scales=None, block: int = 64):
+    """Attention forward through fa_fwd_ex.  Returns (o, lse) (lse None if return_lse is False).
+
+    fp8 inputs (torch.float8_e4m3fn codes) take ``fp8_scales = (sq, sk, sv)`` float32 tensors of
+    shape [B, H, ceil(N / block)] (or None for unit scales) and produce a bfloat16 output.
+    """
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = DTYPE_CODE[q.dtype]
+    out_dtype = torch.bfloat16 if code == FA_FP8_E4M3 else q.dtype
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    s8 = None
+    keep = []
+    if code == FA_FP8_E4M3 and fp8_scales is not None:
+        sq, sk, sv = (t.contiguous() for t in fp8_scales)
+        keep = [sq, sk, sv]
+        s8 = ctypes.pointer(_Fp8Scales(sq.data_ptr(), sk.data_ptr(), sv.data_ptr(), int(block)))
+    st = lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse if return_lse else None),
+                         B, H, N, d, int(bool(causal)), float(scale), code, s8, _stream(q.device))
+    del keep
+    _check(st, "fa_fwd_ex")
+    return out, (lse if return_lse else None)
+
+
+def fp8_prep(x, signs=None, block: int = 64, out=None, scales=None):
+    """Block absmax e4m3 quantisation of x [B, H, N, d] (or [BH, N, d]) through fa_fp8_prep.
+
+    signs: None or a length-d sequence of +1/-1 (host values) for the Hadamard rotation.
+    Returns (codes as torch.float8_e4m3fn, scales float32 [..., ceil(N / block)]).
+    """
+    if not x.is_cuda or not x.is_contiguous() or x.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+        raise ValueError("x must be a contiguous float32/float16/bfloat16 GPU tensor")
+    if x.dim() < 3:
+        raise ValueError("x must be [..., N, d]")
+    N, d = x.shape[-2], x.shape[-1]
+    BH = x.numel() // max(1, N * d) if N * d else int(math.prod(x.shape[:-2]))
+    nblk = -(-N // block) if block > 0 else 0
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    if scales is None:
+        scales = torch.empty(tuple(x.shape[:-2]) + (max(nblk, 0),), dtype=torch.float32, device=x.device)
+    sign_buf = None
+    if signs is not None:
+        sign_list = [int(s) for s in (signs.tolist() if hasattr(signs, "tolist") else signs)]
+        sign_buf = (ctypes.c_int8 * len(sign_list))(*sign_list)
+    st = lib().fa_fp8_prep(_ptr(x), DTYPE_CODE[x.dtype], _ptr(out), _ptr(scales),
+                           ctypes.cast(sign_buf, ctypes.c_void_p) if sign_buf is not None else None,
+                           int(block), int(BH), int(N), int(d), _stream(x.device))
+    _check(st, "fa_fp8_prep")
+    return out, scales

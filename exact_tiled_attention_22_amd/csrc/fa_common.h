@@ -1,0 +1,109 @@
+// fa_common.h — device-side helpers shared by the attention kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+// 32-bit LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const FA_LDS void*)p;
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier for the LDS pipeline.  Unlike __syncthreads() it does not wait for outstanding
+// vector-memory loads (the prefetch of the next tile must stay in flight across it); callers wait
+// for their own direct-to-LDS loads with wait_vmcnt first.  Pending LDS reads are drained, and the
+// "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Value of lane (l ^ 32): the other half of the wave.
+__device__ __forceinline__ float swap_halves(float x) {
+    return __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest-even packing of 8 floats into the MFMA operand of type T.
+template <typename T> struct Vec;
+template <> struct Vec<__bf16> {
+    typedef bf16x8 x8;
+    typedef bf16x4 x4;
+    __device__ static __forceinline__ x8 pack(const float* f) {
+        x8 r;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = (__bf16)f[i];
+        return r;
+    }
+    __device__ static __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ x4 read_tr(const void* lds) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FA_LDS x4*)lds);
+    }
+};
+template <> struct Vec<_Float16> {
+    typedef f16x8 x8;
+    typedef f16x4 x4;
+    __device__ static __forceinline__ x8 pack(const float* f) {
+        x8 r;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = (_Float16)f[i];
+        return r;
+    }
+    __device__ static __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ x4 read_tr(const void* lds) {
+        typedef __fp16 h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+        return __builtin_bit_cast(x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((FA_LDS h4*)lds));
+    }
+};
+
+// Work partition: block id -> (head slice bh, query tile qt).
+// Consecutive block ids are dispatched round-robin over the 8 XCDs (each with its own L2), so when
+// B*H is a multiple of 8 every XCD is given whole heads: all query tiles of a head then read that
+// head's K/V through one L2.  Causal grids run the longest query tiles (most key tiles) first.
+__device__ __forceinline__ void map_block(int bid, int BH, int ntq, bool causal, int& bh, int& qt) {
+    if ((BH & 7) == 0) {
+        const int xcd = bid & 7, slot = bid >> 3, hpx = BH >> 3;
+        if (causal) {
+            qt = ntq - 1 - slot / hpx;
+            bh = xcd * hpx + slot % hpx;
+        } else {
+            bh = xcd * hpx + slot / ntq;
+            qt = slot % ntq;
+        }
+    } else if (causal) {
+        qt = ntq - 1 - bid / BH;
+        bh = bid % BH;
+    } else {
+        bh = bid / ntq;
+        qt = bid % ntq;
+    }
+}
+
+}  // namespace fa

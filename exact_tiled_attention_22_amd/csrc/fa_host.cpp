@@ -1,0 +1,179 @@
+// fa_host.cpp — the C ABI declared in include/fa.h: argument validation, kernel selection, launch.
+//
+// Validation runs before any HIP call, so an invalid request returns its status without touching
+// the device.  No exception crosses the ABI; errors are reported through the return status and a
+// thread-local message (fa_last_error).
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "fa_launch.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+int elem_bytes(int dtype) {
+    switch (dtype) {
+        case FA_F32: return 4;
+        case FA_F16: return 2;
+        case FA_BF16: return 2;
+        case FA_FP8_E4M3: return 1;
+        default: return 0;
+    }
+}
+
+// B*H*N*d must stay well inside int64 and every index the kernels form from (B*H, N) in int32.
+int check_sizes(long long BH, long long N, long long d) {
+    if (BH > 0x7fffffffLL) return fail(FA_ERR_SHAPE, "B*H = %lld exceeds 2^31-1", BH);
+    if (N > 0x7fffffffLL / 1024) return fail(FA_ERR_SHAPE, "N = %lld too large", N);
+    const double total = static_cast<double>(BH) * static_cast<double>(N) * static_cast<double>(d);
+    if (total > 4.0e18) return fail(FA_ERR_SHAPE, "B*H*N*d = %.3g exceeds 2^62", total);
+    return FA_OK;
+}
+
+int from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return FA_OK;
+    if (e == hipErrorNotSupported) return fail(FA_ERR_UNSUPPORTED, "%s: no kernel instance for this request", what);
+    return fail(FA_ERR_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_last_error(void) { return g_err; }
+
+const char* fa_status_str(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+        case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative or overflowing sizes";
+        case FA_ERR_DTYPE: return "FA_ERR_DTYPE: unknown dtype";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: valid request not implemented by this build";
+        case FA_ERR_ALIGN: return "FA_ERR_ALIGN: pointer not 16-byte aligned";
+        case FA_ERR_ARG: return "FA_ERR_ARG: invalid argument";
+        case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";
+        default: return "unknown fa_status";
+    }
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+              int causal, float scale, int dtype, const fa_fp8_scales* s8, void* stream) {
+    g_err[0] = '\0';
+    const int eb = elem_bytes(dtype);
+    if (eb == 0) return fail(FA_ERR_DTYPE, "dtype code %d is not one of FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3", dtype);
+    if (B < 0 || H < 0 || N < 0) return fail(FA_ERR_SHAPE, "negative size B=%d H=%d N=%d", B, H, N);
+    if (causal != 0 && causal != 1) return fail(FA_ERR_ARG, "causal must be 0 or 1, got %d", causal);
+    if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale must be finite");
+    if (d != 64 && d != 128 && d != 256) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128, 256)", d);
+    const long long BH = static_cast<long long>(B) * H;
+    if (BH == 0 || N == 0) return FA_OK;
+    if (int st = check_sizes(BH, N, d)) return st;
+    if (!q || !k || !v || !o) return fail(FA_ERR_NULL, "q, k, v and o must be non-NULL");
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+        return fail(FA_ERR_ALIGN, "q, k, v, o, lse must be 16-byte aligned");
+    const size_t in_bytes = static_cast<size_t>(BH) * N * d * eb;
+    const size_t out_bytes = static_cast<size_t>(BH) * N * d * (dtype == FA_FP8_E4M3 ? 2 : eb);
+    if (overlaps(o, out_bytes, q, in_bytes) || overlaps(o, out_bytes, k, in_bytes) || overlaps(o, out_bytes, v, in_bytes))
+        return fail(FA_ERR_ARG, "o must not overlap q, k or v");
+    if (lse && overlaps(lse, static_cast<size_t>(BH) * N * 4, o, out_bytes))
+        return fail(FA_ERR_ARG, "lse must not overlap o");
+
+    // softmax in base 2: p = 2^(s*c - m) with c = |scale| * log2(e); a negative scale negates Q.
+    // c is kept >= 1e-30 so that masked scores (-inf) times c stay -inf; for |scale| below that the
+    // result is the same as for scale 0 in float32 (every weight rounds to 1).
+    float c = static_cast<float>(std::fabs(static_cast<double>(scale)) * 1.4426950408889634);
+    if (!(c >= 1e-30f)) c = 1e-30f;
+    const bool qneg = std::signbit(scale);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int bh = static_cast<int>(BH);
+
+    switch (dtype) {
+        case FA_F32:
+            return from_hip(fa::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                               static_cast<const float*>(v), static_cast<float*>(o), lse, bh, N, d,
+                                               causal != 0, c, qneg, st),
+                            "fa_fwd(f32)");
+        case FA_F16:
+        case FA_BF16:
+            return from_hip(fa::launch_fwd_16(dtype == FA_BF16, q, k, v, o, lse, bh, N, d, causal != 0, c,
+                                              qneg ? 0x80008000u : 0u, st),
+                            dtype == FA_BF16 ? "fa_fwd(bf16)" : "fa_fwd(f16)");
+        case FA_FP8_E4M3: {
+            const float *sq = nullptr, *sk = nullptr, *sv = nullptr;
+            if (s8) {
+                if (s8->block != 64) return fail(FA_ERR_UNSUPPORTED, "fp8 scale block %d (supported: 64)", s8->block);
+                if (!s8->q_scale || !s8->k_scale || !s8->v_scale)
+                    return fail(FA_ERR_NULL, "fp8 scales: q_scale, k_scale and v_scale must be non-NULL");
+                if (misaligned(s8->q_scale) || misaligned(s8->k_scale) || misaligned(s8->v_scale))
+                    return fail(FA_ERR_ALIGN, "fp8 scale arrays must be 16-byte aligned");
+                sq = s8->q_scale;
+                sk = s8->k_scale;
+                sv = s8->v_scale;
+            }
+            return from_hip(fa::launch_fwd_fp8(q, k, v, o, lse, sq, sk, sv, bh, N, d, causal != 0, c, qneg, st),
+                            "fa_fwd(fp8)");
+        }
+        default:
+            return fail(FA_ERR_DTYPE, "dtype code %d", dtype);
+    }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d, int causal,
+           float scale, int dtype, void* stream) {
+    return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, nullptr, stream);
+}
+
+int fa_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, const int8_t* hadamard, int block, int BH, int N,
+                int d, void* stream) {
+    g_err[0] = '\0';
+    if (x_dtype != FA_F32 && x_dtype != FA_F16 && x_dtype != FA_BF16)
+        return fail(FA_ERR_DTYPE, "fa_fp8_prep input dtype %d (supported: FA_F32, FA_F16, FA_BF16)", x_dtype);
+    if (BH < 0 || N < 0) return fail(FA_ERR_SHAPE, "negative size BH=%d N=%d", BH, N);
+    if (block < 1 || block > 1024) return fail(FA_ERR_ARG, "block must be in 1..1024, got %d", block);
+    if (d != 64 && d != 128 && d != 256) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128, 256)", d);
+    uint64_t bits[4] = {0, 0, 0, 0};
+    if (hadamard) {
+        for (int t = 0; t < d; ++t) {
+            if (hadamard[t] == -1)
+                bits[t >> 6] |= uint64_t{1} << (t & 63);
+            else if (hadamard[t] != 1)
+                return fail(FA_ERR_ARG, "hadamard[%d] = %d; signs must be +1 or -1", t, static_cast<int>(hadamard[t]));
+        }
+    }
+    if (BH == 0 || N == 0) return FA_OK;
+    if (int st = check_sizes(BH, N, d)) return st;
+    if (!x || !x8 || !scales) return fail(FA_ERR_NULL, "x, x8 and scales must be non-NULL");
+    if (misaligned(x) || misaligned(x8) || misaligned(scales))
+        return fail(FA_ERR_ALIGN, "x, x8 and scales must be 16-byte aligned");
+    const int code = x_dtype == FA_F32 ? 0 : x_dtype == FA_F16 ? 1 : 2;
+    return from_hip(fa::launch_fp8_prep(x, code, x8, scales, hadamard != nullptr, bits, block, BH, N, d,
+                                        reinterpret_cast<hipStream_t>(stream)),
+                    "fa_fp8_prep");
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// fa_launch.h — internal launchers between the C ABI (fa_host.cpp) and the HIP kernels.
+// Inputs are already validated by the caller; each launcher only picks the kernel instance and
+// enqueues it.  Returns hipSuccess, or the launch error reported by the runtime, or
+// hipErrorInvalidValue when no instance exists for the request.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// 16-bit float path (bf16 or fp16): v_mfma_f32_32x32x16_{bf16,f16}.
+// c = |scale| * log2(e) (> 0), qflip = 0x80008000 to negate Q (negative scale) else 0.
+hipError_t launch_fwd_16(bool is_bf16, const void* q, const void* k, const void* v, void* o, float* lse,
+                         int BH, int N, int d, bool causal, float c, uint32_t qflip, hipStream_t stream);
+
+// float32 path: v_mfma_f32_32x32x2_f32.  c as above; qneg negates Q.
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int BH, int N, int d, bool causal, float c, bool qneg, hipStream_t stream);
+
+// fp8 e4m3 path (bf16 output).  Scales may be NULL (unit scales).  block must be 64.
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const float* sq, const float* sk, const float* sv,
+                          int BH, int N, int d, bool causal, float c, bool qneg, hipStream_t stream);
+
+// fp8 prep: x_dtype 0 = f32, 1 = f16, 2 = bf16.  sign_bits: bit t set = sign -1 at column t
+// (4 x 64-bit words cover d <= 256).  rotate == false ignores sign_bits.
+hipError_t launch_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, bool rotate,
+                           const uint64_t sign_bits[4], int block, int BH, int N, int d,
+                           hipStream_t stream);
+
+}  // namespace fa

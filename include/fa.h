@@ -1,0 +1,130 @@
+/*
+ * fa.h — C ABI of the exact tiled attention library for AMD Instinct MI355X (gfx950).
+ *
+ * Operation.  For every batch b < B and head h < H the forward pass computes
+ *     O[b,h] = softmax(scale * Q[b,h] * K[b,h]^T  [+ causal mask]) * V[b,h]
+ *     lse[b,h,i] = ln sum_j exp(scale * q_i . k_j)       (over the keys visible to query i)
+ * exactly in real arithmetic, without ever storing the N x N score matrix: query tiles stay in
+ * registers, key/value tiles stream through on-chip LDS and an online softmax keeps a running row
+ * maximum and sum that are corrected at every tile boundary.  Sources: "FlashAttention 2 + 3 —
+ * speicherbewusste Attention-Kernels", sections "Kernpunkte" (same output as softmax(QK^T/sqrt d)V,
+ * tiles of 64-128 rows, online softmax, no N x N matrix in HBM) and "Begriffe auf dieser Seite"
+ * (entry "Online-Softmax": running maximum and a correction factor at each tile boundary).
+ * The causal mask (key j visible to query i iff j <= i) and the lse output are not on the pages;
+ * they are this library's contract.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the library allocates nothing
+ *     and keeps no state between calls except a thread-local error string.
+ *   - Tensors are contiguous row-major [B, H, N, d] (lse: [B, H, N], float32).  N_q = N_k = N.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL = the null
+ *     stream).  No call synchronises the host.  Calls are thread-safe.
+ *   - Arguments are validated before anything is enqueued: a non-FA_OK return means no work was
+ *     launched.  fa_last_error() then describes the problem.  A launch failure reported by the HIP
+ *     runtime returns FA_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     synchronisation.  NaN/Inf tensor contents are not checked.
+ *   - Pointers must be 16-byte aligned (FA_ERR_ALIGN); B, H, N >= 0 with B*H*N == 0 a no-op
+ *     returning FA_OK; supported head dimensions d are 64, 128 and 256 (FA_ERR_UNSUPPORTED).
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+    FA_F32 = 0,      /* float32 in, float32 out */
+    FA_F16 = 1,      /* IEEE binary16 in, binary16 out */
+    FA_BF16 = 2,     /* bfloat16 in, bfloat16 out */
+    FA_FP8_E4M3 = 3  /* OCP e4m3fn bytes in (see fa_fp8_prep), bfloat16 out */
+} fa_dtype;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,        /* a required pointer is NULL */
+    FA_ERR_SHAPE = 2,       /* negative or overflowing sizes */
+    FA_ERR_DTYPE = 3,       /* unknown dtype code */
+    FA_ERR_UNSUPPORTED = 4, /* valid request this build does not implement (e.g. d not in {64,128,256}) */
+    FA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+    FA_ERR_ARG = 6,         /* other invalid argument (non-finite scale, causal not 0/1, bad signs) */
+    FA_ERR_HIP = 7          /* the HIP runtime rejected a launch */
+} fa_status;
+
+/*
+ * Per-block dequantisation scales of the FP8 path, as written by fa_fp8_prep: DEVICE pointers to
+ * float32 arrays [B*H, ceil(N/block)].  Element t of row bh multiplies rows t*block .. t*block+block-1
+ * of that (b,h) slice.  The forward kernel supports block == 64 only.
+ */
+typedef struct {
+    const float* q_scale;
+    const float* k_scale;
+    const float* v_scale;
+    int block;
+} fa_fp8_scales;
+
+/*
+ * Attention forward.
+ *   q, k, v : [B,H,N,d] inputs of type `dtype` (FA_F32, FA_F16 or FA_BF16; FA_FP8_E4M3 means unit
+ *             scales, i.e. fa_fwd_ex with s8 == NULL).
+ *   o       : [B,H,N,d] output, same type as the inputs (bfloat16 for FA_FP8_E4M3).  Must not alias
+ *             q, k or v.
+ *   lse     : [B,H,N] float32 natural-log log-sum-exp per query row, or NULL to skip it.
+ *   causal  : 0 = every key visible; 1 = key j visible to query i iff j <= i.
+ *   scale   : finite float32 multiplier of q.k (callers normally pass 1/sqrt(d)).
+ * Returns an fa_status.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, int causal, float scale, int dtype, void* stream);
+
+/*
+ * Attention forward with FP8 (e4m3) operands and per-block scales (FlashAttention-3 article,
+ * "Drei technische Hebel", item 3 "FP8-Blockquantisierung": blockwise 8-bit operands).
+ * Identical to fa_fwd for other dtypes (s8 is then ignored).  For FA_FP8_E4M3 the inputs are e4m3
+ * codes; the value of element [b,h,n,:] is code * scale[b*H+h][n / block].  s8 == NULL means all
+ * scales are 1.  Scores and the P*V product accumulate in float32; P is rounded to e4m3 for the
+ * second product; o is bfloat16.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int N, int d, int causal, float scale, int dtype,
+              const fa_fp8_scales* s8, void* stream);
+
+/*
+ * Block absmax quantisation to OCP e4m3fn with an optional Hadamard rotation of the head dimension
+ * (FlashAttention-3 article, "Drei technische Hebel", item 3 and "Praxischeck"/"Präzision": blockwise
+ * eight-bit operands, a Hadamard transform to reduce quantisation error; concept card "Kernpunkte":
+ * absmax scaling).
+ *   x        : DEVICE [BH, N, d] input of type x_dtype (FA_F32, FA_F16 or FA_BF16).
+ *   x8       : DEVICE [BH, N, d] output bytes (e4m3fn codes).
+ *   scales   : DEVICE [BH, ceil(N/block)] float32 output, dequantisation scale per block.
+ *   hadamard : HOST pointer to d int8 values, each +1 or -1 (the random sign vector s), or NULL for
+ *              no rotation.  With signs, each row is replaced by (x * s) H_d / sqrt(d) (H_d the
+ *              Sylvester Hadamard matrix) before quantisation; pass the same signs for Q and K so
+ *              that Q K^T is preserved.  Requires d to be a power of two.
+ *   block    : rows per scale block, 1..1024 (64 for the forward kernel).
+ * Per block: amax = max |x'|, scale = amax/448, code = e4m3_RNE(x' * (448/amax)) computed in float32
+ * (the rotation as float32 butterflies with strides 1, 2, ..., d/2 followed by a multiply with the
+ * float32 value of 1/sqrt(d)); an all-zero block stores scale 1 and zero codes.
+ */
+int fa_fp8_prep(const void* x, int x_dtype, void* x8, float* scales,
+                const int8_t* hadamard, int block, int BH, int N, int d, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* fa_status_str(int status);
+
+/* Detail of the last non-FA_OK return on the calling thread ("" if none).  Valid until the next call
+ * on the same thread. */
+const char* fa_last_error(void);
+
+/* FA_ABI_VERSION of the loaded library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

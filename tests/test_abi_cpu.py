@@ -1,0 +1,102 @@
+"""The C ABI on a host without a GPU: the header is valid C99, the library loads and exports every
+declared symbol, and argument validation returns the documented status before any HIP call.
+No compute call is made here."""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+LIB = os.path.join(ROOT, "exact_tiled_attention_22_amd", "libfa.so")
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_DTYPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_ARG = range(7)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_compiles_as_c99():
+    with tempfile.TemporaryDirectory() as td:
+        src = os.path.join(td, "t.c")
+        with open(src, "w") as f:
+            f.write('#include "fa.h"\nint main(void) { fa_fp8_scales s = {0, 0, 0, 64}; '
+                    'return (int)FA_OK + s.block * 0 + (int)sizeof(&fa_fwd) * 0; }\n')
+        r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", "-I", os.path.dirname(HEADER),
+                            src, "-c", "-o", os.path.join(td, "t.o")], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libfa.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert set(names) == {"fa_fwd", "fa_fwd_ex", "fa_fp8_prep", "fa_status_str", "fa_last_error",
+                          "fa_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", nm, re.M), f"{n} not exported with C linkage"
+
+
+def _fwd(lib, q=16, k=16, v=16, o=16, lse=None, B=1, H=1, N=8, d=128, causal=0, scale=0.1, dtype=2):
+    f = lib.fa_fwd
+    f.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, vp, vp, vp, vp] + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int, vp]
+    return f(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, None)
+
+
+def test_validation_statuses(lib):
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_abi_version.restype = ctypes.c_int
+    assert lib.fa_abi_version() == 1
+    big = 1 << 20  # fake, 16-aligned addresses: validation never dereferences them
+    assert _fwd(lib, dtype=9) == FA_ERR_DTYPE
+    assert _fwd(lib, N=-1) == FA_ERR_SHAPE
+    assert _fwd(lib, causal=2) == FA_ERR_ARG
+    assert _fwd(lib, scale=float("nan")) == FA_ERR_ARG
+    assert _fwd(lib, scale=float("inf")) == FA_ERR_ARG
+    assert _fwd(lib, d=96) == FA_ERR_UNSUPPORTED
+    assert b"d=96" in lib.fa_last_error()
+    assert _fwd(lib, N=0, q=None, k=None, v=None, o=None) == FA_OK  # empty problem: no-op
+    assert _fwd(lib, B=0) == FA_OK
+    assert _fwd(lib, q=None) == FA_ERR_NULL
+    assert _fwd(lib, q=big + 8, k=big * 2, v=big * 3, o=big * 4) == FA_ERR_ALIGN
+    assert _fwd(lib, q=big, k=big * 2, v=big * 3, o=big * 4, lse=big * 5 + 4) == FA_ERR_ALIGN
+    assert _fwd(lib, q=big, k=big * 2, v=big * 3, o=big) == FA_ERR_ARG  # o aliases q
+    assert _fwd(lib, B=1 << 16, H=1 << 16, q=big, k=big * 2, v=big * 3, o=big * 4) == FA_ERR_SHAPE
+    for s in range(8):
+        assert lib.fa_status_str(s)
+    assert lib.fa_status_str(99) == b"unknown fa_status"
+
+
+def test_prep_validation_statuses(lib):
+    f = lib.fa_fp8_prep
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, ctypes.c_int, vp, vp, vp] + [ctypes.c_int] * 4 + [vp]
+    f.restype = ctypes.c_int
+    big = 1 << 20
+    good = (ctypes.c_int8 * 128)(*([1, -1] * 64))
+    bad = (ctypes.c_int8 * 128)(*([1] * 127 + [0]))
+    assert f(big, 3, big * 2, big * 3, None, 64, 1, 64, 128, None) == FA_ERR_DTYPE
+    assert f(big, 2, big * 2, big * 3, None, 0, 1, 64, 128, None) == FA_ERR_ARG
+    assert f(big, 2, big * 2, big * 3, None, 64, 1, 64, 96, None) == FA_ERR_UNSUPPORTED
+    assert f(big, 2, big * 2, big * 3, ctypes.cast(bad, vp), 64, 1, 64, 128, None) == FA_ERR_ARG
+    assert f(big, 2, big * 2, big * 3, ctypes.cast(good, vp), 64, 0, 64, 128, None) == FA_OK
+    assert f(None, 2, big * 2, big * 3, ctypes.cast(good, vp), 64, 1, 64, 128, None) == FA_ERR_NULL
+    assert f(big + 4, 2, big * 2, big * 3, None, 64, 1, 64, 128, None) == FA_ERR_ALIGN
