@@ -112,9 +112,11 @@ def test_invariants_on_gpu(dtype):
 
 
 def test_zero_and_negative_scale():
+    # a negative scale flips the sign of every score (the kernel negates Q); scale 0 gives uniform
+    # weights.  |scale| = 1/sqrt(d) keeps the scores N(0,1) as the tolerance assumes.
     N, d = 150, 128
     q, k, v = gen_qkv(1, 2, N, d, "bf16", seed=11)
-    for scale in (0.0, -0.3):
+    for scale in (0.0, -_f32(1 / math.sqrt(d))):
         o, lse = _run(q, k, v, True, scale)
         o_ref, lse_ref = attention_ref(q, k, v, True, scale)
         _compare(o, lse, o_ref, lse_ref, f"scale={scale}")
