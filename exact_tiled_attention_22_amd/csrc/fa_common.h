@@ -45,6 +45,25 @@ __device__ __forceinline__ float swap_halves(float x) {
     return __shfl_xor(x, 32, 64);
 }
 
+// max / sum of x over lanes l and l ^ 32 (gfx950 v_permlane32_swap: the upper half of the first
+// register trades places with the lower half of the second).
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One 16-byte direct HBM->LDS copy per lane: lane l writes LDS bytes [m0 + 16 l, m0 + 16 l + 16).
+// Issued as inline assembly so that the compiler does not treat the in-flight copy as a pending
+// LDS write (it would otherwise wait for every outstanding copy before each LDS read); the
+// caller waits with wait_vmcnt before a barrier.  lds_base must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Round-to-nearest-even packing of 8 floats into the MFMA operand of type T.
