@@ -50,6 +50,47 @@ def load_traffic(cfg_id: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20
+
+
+def ingest_counters(cfg_id: int, fetch_csv: str, write_csv: str) -> int:
+    """HBM bytes per attention launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (KiB per
+    dispatch), each scaled by the same counter on a plain copy of COPY_BYTES (which reads and writes
+    exactly COPY_BYTES)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return vals
+
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = per_kernel(path, counter)
+        attn = [v for k, v in vals.items() if "fa_fwd" in k]
+        copy = [v for k, v in vals.items() if "copyBuffer" in k]
+        if not attn or not copy:
+            raise SystemExit(f"{path}: need attention and copy dispatches, found {list(vals)}")
+        attn_kib = sum(attn[0]) / len(attn[0])
+        copy_kib = sum(copy[0]) / len(copy[0])
+        factor = (COPY_BYTES / 1024.0) / copy_kib
+        out[counter] = {"attention_kib_per_dispatch": attn_kib, "copy_kib_per_dispatch": copy_kib,
+                        "copy_scale_factor": factor, "bytes_per_launch": attn_kib * 1024.0 * factor}
+    rec = {"config": cfg_id, "kernel_source_sha256_16": kernel_source_hash(),
+           "counters": out,
+           "hbm_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]}
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"traffic_cfg{cfg_id}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+    return 0
+
+
 def cpu_baseline(w, seed: int, budget_s: float = 12.0):
     """Time the float64 oracle on whole heads of the workload until ~budget_s of CPU work."""
     import numpy as np
@@ -75,7 +116,7 @@ def cpu_baseline(w, seed: int, budget_s: float = 12.0):
             attention_rows(q[0, h], k[0, h], v[0, h], rows, w.causal, w.scale)
         heads += 1
         done_flops += per_head
-        if time.perf_counter() - t0 >= budget_s or heads >= 64:
+        if time.perf_counter() - t0 >= budget_s or heads >= 512:
             break
     dt = time.perf_counter() - t0
     return {
@@ -95,7 +136,14 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) "
+                         "into profiles/traffic_cfg<N>.json and exit")
     args = ap.parse_args()
+    if args.ingest_counters:
+        return ingest_counters(args.config, *args.ingest_counters)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the (b,h) slices would "
               "shard across GPUs with no communication, but no multi-GPU run is part of this build.",
@@ -178,6 +226,12 @@ def main() -> int:
             "kernel_avg_ms": round(avg_launch_ms, 5),
         },
     }
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, seed)
     print(json.dumps(line), flush=True)
