@@ -4,7 +4,15 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_ref, fp8_attention_ref, fp8_prep_ref
+from oracle import (
+    attention_ref,
+    attention_rows,
+    dequantize_blocks,
+    e4m3_decode,
+    e4m3_encode,
+    fp8_attention_ref,
+    fp8_prep_ref,
+)
 from synth import CONFIGS, gen_fp8_workload, gen_qkv, gen_signs
 
 pytestmark = pytest.mark.gpu
@@ -44,3 +52,96 @@ def test_prep_other_blocks_and_zero_block(block):
     c_ref, s_ref = fp8_prep_ref(q, gen_signs(128, 3), block)
     np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
     np.testing.assert_array_equal(codes.view(torch.uint8).cpu().numpy(), c_ref)
+
+
+def _rmse(a, b):
+    return float(np.sqrt(np.mean((np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64)) ** 2)))
+
+
+def _fp8_case(B, H, N, d, causal, seed, outliers=True, scale=None):
+    fa = _fa()
+    frac, mult = (0.001, 20.0) if outliers else (0.0, 1.0)
+    q, k, v = gen_qkv(B, H, N, d, "bf16", seed=seed, outlier_frac=frac, outlier_mult=mult)
+    signs = gen_signs(d, seed=seed)
+    scale = float(np.float32(1 / np.sqrt(d))) if scale is None else scale
+    dev = torch.device("cuda")
+    q8, sq = fa.fp8_prep(q.to(dev), signs, 64)
+    k8, sk = fa.fp8_prep(k.to(dev), signs, 64)
+    v8, sv = fa.fp8_prep(v.to(dev), None, 64)
+    o, lse = fa.fwd(q8, k8, v8, causal=causal, scale=scale, fp8_scales=(sq, sk, sv))
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    # oracle (i): its own quantisation of the same bf16 inputs, then float64 attention
+    cq, csq = fp8_prep_ref(q, signs, 64)
+    ck, csk = fp8_prep_ref(k, signs, 64)
+    cv, csv = fp8_prep_ref(v, None, 64)
+    o_i, lse_i = fp8_attention_ref(cq, csq, ck, csk, cv, csv, 64, causal, scale)
+    o_ii, _ = attention_ref(q, k, v, causal, scale)  # (ii): original inputs
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    r_i, r_ii = _rmse(o, o_i), _rmse(o, o_ii)
+    floor = _rmse(o_i, o_ii)
+    dl = float(np.abs(lse - lse_i).max())
+    print(f"fp8 B{B} H{H} N{N} d{d} causal={causal}: RMSE vs dequantised-input oracle {r_i:.3e}, "
+          f"vs original inputs {r_ii:.3e} (format floor {floor:.3e}), max|dlse| {dl:.2e}", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    return r_i, r_ii, dl
+
+
+@pytest.mark.parametrize("N,d,causal", [(200, 128, False), (333, 128, True), (64, 64, False), (130, 64, True),
+                                        (256, 256, False), (300, 256, True), (1, 128, False)])
+def test_fp8_forward_rmse(N, d, causal):
+    r_i, _, dl = _fp8_case(1, 2, N, d, causal, seed=N + d)
+    assert r_i <= 3e-2
+    assert dl <= 1e-3
+
+
+def test_fp8_forward_unit_scales_and_negative_scale():
+    fa = _fa()
+    # codes used directly (no scales): value = code; N(0,1) values rounded to e4m3 keep the contract
+    rng = np.random.default_rng(3)
+    codes = [e4m3_encode(rng.standard_normal((1, 1, 150, 128))) for _ in range(3)]
+    t = [torch.from_numpy(c).view(torch.float8_e4m3fn).cuda() for c in codes]
+    s0 = float(np.float32(1 / np.sqrt(128)))
+    for scale in (s0, -s0):
+        o, lse = fa.fwd(*t, causal=False, scale=scale)
+        torch.cuda.synchronize()
+        vals = [e4m3_decode(c) for c in codes]
+        o_ref, lse_ref = attention_ref(*vals, False, scale)
+        r = _rmse(o.float().cpu().numpy(), o_ref)
+        print(f"fp8 unit scales scale={scale}: RMSE {r:.3e}", flush=True)
+        assert r <= 3e-2 and float(np.abs(lse.cpu().numpy() - lse_ref).max()) <= 1e-3
+
+
+def test_fp8_full_config5_sampled_rows():
+    fa = _fa()
+    w = CONFIGS[5]
+    q, k, v, signs = gen_fp8_workload(w)
+    dev = torch.device("cuda")
+    q8, sq = fa.fp8_prep(q.to(dev), signs, 64)
+    k8, sk = fa.fp8_prep(k.to(dev), signs, 64)
+    v8, sv = fa.fp8_prep(v.to(dev), None, 64)
+    o, lse = fa.fwd(q8, k8, v8, causal=w.causal, scale=w.scale, fp8_scales=(sq, sk, sv))
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    rng = np.random.default_rng(55)
+    err_i, err_ii, worst_l = [], [], 0.0
+    for bh in rng.choice(w.B * w.H, size=3, replace=False):
+        b, h = divmod(int(bh), w.H)
+        cq, csq = fp8_prep_ref(q[b, h][None], signs, 64)
+        ck, csk = fp8_prep_ref(k[b, h][None], signs, 64)
+        cv, csv = fp8_prep_ref(v[b, h][None], None, 64)
+        qd, kd, vd = (dequantize_blocks(c, s_, 64)[0] for c, s_ in ((cq, csq), (ck, csk), (cv, csv)))
+        rows = np.unique(np.concatenate([[0, w.N - 1], rng.integers(0, w.N, 62)]))
+        o_i, lse_i = attention_rows(qd, kd, vd, rows, w.causal, w.scale)
+        o_ii, _ = attention_rows(q[b, h], k[b, h], v[b, h], rows, w.causal, w.scale)
+        err_i.append(o[b, h][rows] - o_i)
+        err_ii.append(o[b, h][rows] - o_ii)
+        worst_l = max(worst_l, float(np.abs(lse[b, h][rows] - lse_i).max()))
+    r_i = float(np.sqrt(np.mean(np.concatenate(err_i) ** 2)))
+    r_ii = float(np.sqrt(np.mean(np.concatenate(err_ii) ** 2)))
+    print(f"{w.name}: sampled RMSE vs dequantised-input oracle {r_i:.3e}, vs original inputs {r_ii:.3e}, "
+          f"max|dlse| {worst_l:.2e}", flush=True)
+    assert np.isfinite(o).all()
+    assert r_i <= 3e-2 and worst_l <= 1e-3
