@@ -32,7 +32,7 @@ namespace {
 
 constexpr float kTau = 8.0f;  // rescale only when the running maximum grows by more than 2^8
 
-template <int D, int QB, int NW>
+template <int D, int QB, int NW, int WPC>
 struct Tile {
     static constexpr int BN = 64;                 // keys per tile
     static constexpr int QW = 32 * QB;            // query rows per wave
@@ -45,39 +45,43 @@ struct Tile {
     static constexpr int Q_CHUNKS = BM * CPR;
     static constexpr int QLPT = Q_CHUNKS / THREADS;
     static constexpr int Q_BYTES = Q_CHUNKS * 16;
-    // the Q staging area gets its own LDS region when it fits, otherwise it aliases stage 1 (K1|V1)
-    static constexpr bool Q_SEPARATE = Q_BYTES + 4 * KV_BYTES <= 160 * 1024;
+    // WPC workgroups share a CU's 160 KiB of LDS.  The Q staging area gets its own region after the
+    // K/V stages when that still fits, otherwise it aliases stage 1 (K1|V1) during the prologue.
+    static constexpr int LDS_LIMIT = 160 * 1024 / WPC;
+    static constexpr bool Q_SEPARATE = Q_BYTES + 4 * KV_BYTES <= LDS_LIMIT;
     static constexpr int LDS_BYTES = Q_SEPARATE ? Q_BYTES + 4 * KV_BYTES : 4 * KV_BYTES;
+    static constexpr int OFF_K0 = 0, OFF_V0 = KV_BYTES, OFF_K1 = 2 * KV_BYTES, OFF_V1 = 3 * KV_BYTES;
+    static constexpr int OFF_Q = Q_SEPARATE ? 4 * KV_BYTES : OFF_K1;
     static_assert(CHUNKS % THREADS == 0 && Q_CHUNKS % THREADS == 0, "tiles split evenly over threads");
     static_assert(Q_SEPARATE || Q_BYTES <= 2 * KV_BYTES, "Q staging must fit in stage 1");
+    static_assert(LDS_BYTES <= LDS_LIMIT, "LDS budget");
     static_assert(LPT <= 16, "vmcnt range");
 };
 
-// XOR swizzle of the 16-byte chunk index inside one LDS row: the eight rows {0,1,2,3,8,9,10,11}
-// (+4) read together by a score-operand fetch, and the four consecutive rows read together by a
-// transposing V fetch, fall into distinct bank groups.
+// XOR swizzle of the 16-byte chunk index inside one LDS row.  The LDS serves 256 bytes per clock
+// (64 banks of 4 bytes = 16 groups of 16 bytes).  Two access patterns must hit 16 distinct groups:
+//   * a score-operand fetch: 16 lanes read one logical chunk of 16 consecutive rows;
+//   * a transposing V fetch: 32 lanes read 4 logical chunks of 4 consecutive rows (row % 4 == 0).
+// Rows of 256 or 512 bytes start in group 0, so the group is the physical chunk mod 16: swapping the
+// two 2-bit halves of (row mod 16) does both.  Rows of 128 bytes alternate between groups 0 and 8, so
+// the parity of the row already separates pairs and 3 bits suffice.
 template <int CPR>
 __device__ __forceinline__ int swz(int row) {
-    int f = ((row & 3) << 1) | ((row >> 3) & 1);
-    if constexpr (CPR >= 16) f |= ((row >> 2) & 1) << 3;
-    return f;
+    if constexpr (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
-template <typename T, int D, int QB, int NW, bool CAUSAL>
+template <typename T, int D, int QB, int NW, int WPC, bool CAUSAL>
 struct Fwd {
-    using TL = Tile<D, QB, NW>;
+    using TL = Tile<D, QB, NW, WPC>;
     using VT = Vec<T>;
     using x8 = typename VT::x8;
     using x4 = typename VT::x4;
     static constexpr int BN = TL::BN, QW = TL::QW, BM = TL::BM, CPR = TL::CPR, LPT = TL::LPT;
     static constexpr int KS = D / 16;  // k-steps of the score product
     static constexpr int CB = D / 32;  // 32-column blocks of the output
-    // LDS map (byte offsets)
-    static constexpr int OFF_K0 = TL::Q_SEPARATE ? TL::Q_BYTES : 0;
-    static constexpr int OFF_V0 = OFF_K0 + TL::KV_BYTES;
-    static constexpr int OFF_K1 = OFF_V0 + TL::KV_BYTES;
-    static constexpr int OFF_V1 = OFF_K1 + TL::KV_BYTES;
-    static constexpr int OFF_Q = TL::Q_SEPARATE ? 0 : OFF_K1;
+    static constexpr int OFF_K0 = TL::OFF_K0, OFF_V0 = TL::OFF_V0, OFF_K1 = TL::OFF_K1, OFF_V1 = TL::OFF_V1;
+    static constexpr int OFF_Q = TL::OFF_Q;
 
     // Copy rows [r0, r0 + ROWS) of a [N, D] slice into an LDS tile (rows >= N read row N-1; they are
     // masked or never stored).  Slot s of the tile holds chunk (s % CPR) ^ swz(row) of row s / CPR.
@@ -94,19 +98,32 @@ struct Fwd {
         }
     }
 
-    // S^T = K_tile Q^T for this wave's QB query blocks (fp32 accumulate)
+    // Per-lane geometry of the MFMA operand fetches inside one LDS tile.
+    struct Lane {
+        int kperm, h;     // score A-operand: row kperm (+32 for the second key block), chunk 2*ks + h
+        int vrow, vcc, vb;  // value A-operand (transposing read): row u*4 + vrow, chunk cb*4 + vcc, byte vb
+        __device__ __forceinline__ int koff(int ks) const {
+            return (kperm * CPR + ((2 * ks + h) ^ swz<CPR>(kperm))) * 16;
+        }
+        __device__ __forceinline__ int voff(int cb, int u) const {
+            const int row = u * 4 + vrow;
+            return (row * CPR + ((cb * 4 + vcc) ^ swz<CPR>(row))) * 16 + vb;
+        }
+    };
+
+    // S^T = K_tile Q^T for this wave's QB query blocks (fp32 accumulate).  The second 32-key block
+    // sits 32 rows further (a compile-time offset).
     static __device__ __forceinline__ void scores(const char* kl, const x8 (&qreg)[QB][KS], f32x16 (&s)[QB][2],
-                                                  int kbase, int h, int ksw) {
+                                                  const Lane& ln) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) s[qb][kb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int xo = ((2 * ks + h) ^ ksw) * 16;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const x8 kop = *(const x8*)(kl + kbase + kb * 32 * CPR * 16 + xo);
+                const x8 kop = *(const x8*)(kl + ln.koff(ks) + kb * 32 * CPR * 16);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) s[qb][kb] = VT::mfma(kop, qreg[qb][ks], s[qb][kb]);
             }
@@ -181,26 +198,156 @@ struct Fwd {
         }
     }
 
-    // O^T += V^T P^T for one tile (V^T operands through transposing LDS reads)
+    // O^T += V^T P^T for one tile (V^T operands through transposing LDS reads); 16-key step s sits
+    // 16 rows further (a compile-time offset).
     static __device__ __forceinline__ void pv(const char* vl, const x8 (&p)[QB][4], f32x16 (&oacc)[QB][CB],
-                                              int vbase_e, int vbase_o) {
+                                              const Lane& ln) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
-                x4 half[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    // 64-byte chunk group after the row's swizzle bit 3 (present when CPR >= 16)
-                    const int cp = cb ^ (CPR >= 16 ? 2 * u : 0);
-                    const int base = (cp & 1) ? vbase_o : vbase_e;
-                    half[u] = VT::read_tr(vl + base + (s * 16 + u * 4) * CPR * 16 + cp * 64);
-                }
-                const x8 vop = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                const x4 lo = VT::read_tr(vl + ln.voff(cb, 0) + s * 16 * CPR * 16);
+                const x4 hi = VT::read_tr(vl + ln.voff(cb, 1) + s * 16 * CPR * 16);
+                const x8 vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) oacc[qb][cb] = VT::mfma(vop, p[qb][s], oacc[qb][cb]);
             }
         }
+    }
+
+    // Instruction order for the scheduler inside one tile's straight-line body: the K operand reads
+    // run a few ahead of the score MFMAs, each score MFMA is followed by softmax VALU work (which does
+    // not depend on it), then the V operand reads run ahead of the value MFMAs.
+    static __device__ __forceinline__ void interleave() {
+        constexpr int NQK = KS * 2 * QB, NKR = KS * 2, NPV = 4 * CB * QB;
+        constexpr int AHEAD = D >= 256 ? 2 : 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // first K reads
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // score MFMA
+            if (i + AHEAD < NKR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next K read
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // softmax VALU
+        }
+        constexpr int VAHEAD = D >= 256 ? 1 : 2;  // value MFMAs whose operands are in flight
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * VAHEAD, 0);
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // value MFMA
+            if (i + VAHEAD < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V^T operand reads
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+    }
+
+    // O = acc / l rounded to T (lane holds 16 columns of its query per 32-column block), and
+    // lse = ln2 * (m + log2 l)
+    static __device__ __forceinline__ void epilogue(T* __restrict__ O, float* __restrict__ LSE, size_t head, int bh,
+                                                    int N, int q0w, int n32, int h, const f32x16 (&oacc)[QB][CB],
+                                                    const float (&m_run)[QB], const float (&l_run)[QB]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float lt = halves_sum(l_run[qb]);
+            const float inv = 1.0f / lt;
+            const int query = q0w + qb * 32 + n32;
+            if (query < N) {
+                T* orow = O + head + (size_t)query * D;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        x4 out;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) out[e] = (T)(oacc[qb][cb][g * 4 + e] * inv);
+                        *(x4*)(orow + cb * 32 + g * 8 + h * 4) = out;
+                    }
+                if (LSE != nullptr && h == 0)
+                    LSE[(size_t)bh * N + query] = (m_run[qb] + __log2f(lt)) * 0.69314718055994531f;
+            }
+        }
+    }
+
+    // In-order pipeline for large head dimensions (one score buffer): iteration j holds K_j and V_j
+    // in stage j % 2 and copies K_{j+1}, V_{j+1} into the other stage; the scores of tile j come first,
+    // then its softmax, whose exponentials interleave with the value MFMAs.  Q is staged through
+    // stage 1 during the prologue.
+    static __device__ __forceinline__ void run_seq(const T* __restrict__ Q, const T* __restrict__ K,
+                                                   const T* __restrict__ V, T* __restrict__ O,
+                                                   float* __restrict__ LSE, int N, int BH, int ntq, float c,
+                                                   uint32_t qflip, char* smem) {
+        static_assert(!TL::Q_SEPARATE, "the in-order pipeline stages Q in stage 1");
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int n32 = lane & 31;
+        const int h = lane >> 5;
+        const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+        int bh, qt;
+        map_block(blockIdx.x, BH, ntq, CAUSAL, bh, qt);
+        const size_t head = (size_t)bh * N * D;
+        const T* Qh = Q + head;
+        const T* Kh = K + head;
+        const T* Vh = V + head;
+        const int q0 = qt * BM;
+        const int q0w = q0 + wave * QW;
+        const int nt = ((CAUSAL ? min(N, q0 + BM) : N) + BN - 1) / BN;
+        const int ntw = ((CAUSAL ? min(N, q0w + QW) : N) + BN - 1) / BN;
+        Lane ln;
+        ln.kperm = ((n32 >> 4) & 1) * 16 + ((n32 >> 2) & 1) * 8 + ((n32 >> 3) & 1) * 4 + (n32 & 3);
+        ln.h = h;
+        {
+            const int i16 = lane & 15, G = lane >> 4;
+            ln.vrow = (G >> 1) * 8 + (i16 >> 2);
+            ln.vcc = (G & 1) * 2 + ((i16 & 3) >> 1);
+            ln.vb = (i16 & 1) * 8;
+        }
+        copy_rows<TL::QLPT>(Qh, q0, N, lbase + OFF_Q, tid, wave);
+        copy_rows<LPT>(Kh, 0, N, lbase + OFF_K0, tid, wave);
+        copy_rows<LPT>(Vh, 0, N, lbase + OFF_V0, tid, wave);
+        wait_vmcnt<0>();
+        lds_barrier();
+        x8 qreg[QB][KS];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int row = wave * QW + qb * 32 + n32;
+            const char* qrow = smem + OFF_Q + row * CPR * 16;
+            const int qsw = swz<CPR>(row);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                i32x4 raw = *(const i32x4*)(qrow + ((2 * ks + h) ^ qsw) * 16);
+                raw ^= (int)qflip;
+                qreg[qb][ks] = __builtin_bit_cast(x8, raw);
+            }
+        }
+        f32x16 oacc[QB][CB];
+        float m_run[QB], l_run[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            m_run[qb] = -INFINITY;
+            l_run[qb] = 0.0f;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) oacc[qb][cb] = f32x16{};
+        }
+        auto iteration = [&](int j, int ok, int ov, uint32_t dk, uint32_t dv) {
+            wait_vmcnt<0>();
+            lds_barrier();  // K_j, V_j visible; the other stage (and the Q staging) is free
+            if (j + 1 < nt) {
+                copy_rows<LPT>(Kh, (j + 1) * BN, N, lbase + dk, tid, wave);
+                copy_rows<LPT>(Vh, (j + 1) * BN, N, lbase + dv, tid, wave);
+            }
+            if (j < ntw) {
+                f32x16 sc[QB][2];
+                scores(smem + ok, qreg, sc, ln);
+                mask(sc, j * BN, N, q0w, n32, h);
+                update_max(sc, c, oacc, m_run, l_run);
+                x8 p[QB][4];
+                exps(sc, c, m_run, l_run, p);
+                pv(smem + ov, p, oacc, ln);
+            }
+        };
+        for (int j = 0; j < nt; j += 2) {
+            iteration(j, OFF_K0, OFF_V0, OFF_K1, OFF_V1);
+            if (j + 1 < nt) iteration(j + 1, OFF_K1, OFF_V1, OFF_K0, OFF_V0);
+        }
+        epilogue(O, LSE, head, bh, N, q0w, n32, h, oacc, m_run, l_run);
     }
 
     static __device__ __forceinline__ void run(const T* __restrict__ Q, const T* __restrict__ K,
@@ -225,17 +372,15 @@ struct Fwd {
         const int nt = ((CAUSAL ? min(N, q0 + BM) : N) + BN - 1) / BN;   // tiles of the workgroup
         const int ntw = ((CAUSAL ? min(N, q0w + QW) : N) + BN - 1) / BN; // tiles this wave computes
 
-        // per-lane LDS offsets
-        const int kperm = ((n32 >> 4) & 1) * 16 + ((n32 >> 2) & 1) * 8 + ((n32 >> 3) & 1) * 4 + (n32 & 3);
-        const int kbase = kperm * CPR * 16;
-        const int ksw = swz<CPR>(kperm);
-        const int i16 = lane & 15, G = lane >> 4;
-        const int vrow = (G >> 1) * 8 + (i16 >> 2);
-        const int vl_sw = ((i16 >> 2) << 1) | (G >> 1);         // swizzle bits of vrow (bit 2 = u)
-        const int vcc = (G & 1) * 2 + ((i16 & 3) >> 1);          // 16-byte chunk within 32 columns
-        const int b2 = (vl_sw >> 2) & 1;
-        const int vbase = vrow * CPR * 16 + ((vcc ^ vl_sw) & 3) * 16 + (i16 & 1) * 8;
-        const int vbase_e = vbase + 64 * b2, vbase_o = vbase - 64 * b2;
+        Lane ln;
+        ln.kperm = ((n32 >> 4) & 1) * 16 + ((n32 >> 2) & 1) * 8 + ((n32 >> 3) & 1) * 4 + (n32 & 3);
+        ln.h = h;
+        {
+            const int i16 = lane & 15, G = lane >> 4;  // transposing read: lane = 16 G + i
+            ln.vrow = (G >> 1) * 8 + (i16 >> 2);
+            ln.vcc = (G & 1) * 2 + ((i16 & 3) >> 1);
+            ln.vb = (i16 & 1) * 8;
+        }
 
         // ---- prologue: Q, K_0, V_0 (and K_1) into LDS ----
         copy_rows<TL::QLPT>(Qh, q0, N, lbase + OFF_Q, tid, wave);
@@ -278,7 +423,7 @@ struct Fwd {
         }
 
         f32x16 s0[QB][2], s1[QB][2];
-        scores(smem + OFF_K0, qreg, s0, kbase, h, ksw);
+        scores(smem + OFF_K0, qreg, s0, ln);
         if constexpr (!TL::Q_SEPARATE) {
             lds_barrier();  // every wave has its Q operand: stage 1 may be overwritten
             if (nt > 1) copy_rows<LPT>(Kh, BN, N, lbase + OFF_K1, tid, wave);
@@ -294,14 +439,14 @@ struct Fwd {
             if (j < ntw) {
                 mask(cur, j * BN, N, q0w, n32, h);
                 update_max(cur, c, oacc, m_run, l_run);
+                // next tile's scores (its K stage always holds valid data; on the last tile the result is
+                // unused) in the same basic block as this tile's exponentials so the two overlap; with
+                // d = 256 the registers only allow the two in sequence
+                scores(smem + okn, qreg, nxt, ln);
                 x8 p[QB][4];
-                if (j + 1 < ntw) {
-                    scores(smem + okn, qreg, nxt, kbase, h, ksw);
-                    exps(cur, c, m_run, l_run, p);
-                } else {
-                    exps(cur, c, m_run, l_run, p);
-                }
-                pv(smem + ov, p, oacc, vbase_e, vbase_o);
+                exps(cur, c, m_run, l_run, p);
+                pv(smem + ov, p, oacc, ln);
+                interleave();
             }
         };
         for (int j = 0; j < nt; j += 2) {
@@ -310,54 +455,38 @@ struct Fwd {
             if (j + 1 < nt) iteration(j + 1, s1, s0, OFF_K0, OFF_V1, OFF_K1, OFF_V0);
         }
 
-        // ---- epilogue: O = acc / l (rounded to T), lse = ln2 * (m + log2 l) ----
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const float lt = halves_sum(l_run[qb]);
-            const float inv = 1.0f / lt;
-            const int query = q0w + qb * 32 + n32;
-            if (query < N) {
-                T* orow = O + head + (size_t)query * D;
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        x4 out;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) out[e] = (T)(oacc[qb][cb][g * 4 + e] * inv);
-                        *(x4*)(orow + cb * 32 + g * 8 + h * 4) = out;
-                    }
-                if (LSE != nullptr && h == 0)
-                    LSE[(size_t)bh * N + query] = (m_run[qb] + __log2f(lt)) * 0.69314718055994531f;
-            }
-        }
+        epilogue(O, LSE, head, bh, N, q0w, n32, h, oacc, m_run, l_run);
     }
 };
 
-template <typename T, int D, int QB, int NW, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW, 1) void fa_fwd16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                              const T* __restrict__ V, T* __restrict__ O,
-                                                              float* __restrict__ LSE, int N, int BH, int ntq,
-                                                              float c, uint32_t qflip) {
-    __shared__ __attribute__((aligned(1024))) char smem[Tile<D, QB, NW>::LDS_BYTES];
-    Fwd<T, D, QB, NW, CAUSAL>::run(Q, K, V, O, LSE, N, BH, ntq, c, qflip, smem);
+// One workgroup per (b, h, query tile); WPC of them share a CU (2 waves per SIMD in total), so one
+// workgroup's prologue and epilogue overlap the other's tile loop.
+template <typename T, int D, int QB, int NW, int WPC, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW, (NW * WPC) / 4) void fa_fwd16_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
+    float* __restrict__ LSE, int N, int BH, int ntq, float c, uint32_t qflip) {
+    __shared__ __attribute__((aligned(1024))) char smem[Tile<D, QB, NW, WPC>::LDS_BYTES];
+    if constexpr (D <= 128)
+        Fwd<T, D, QB, NW, WPC, CAUSAL>::run(Q, K, V, O, LSE, N, BH, ntq, c, qflip, smem);
+    else
+        Fwd<T, D, QB, NW, WPC, CAUSAL>::run_seq(Q, K, V, O, LSE, N, BH, ntq, c, qflip, smem);
 }
 
-// per head dimension: query blocks per wave and waves per workgroup
+// per head dimension: query blocks per wave, waves per workgroup, workgroups per CU
 template <int D> struct Shape;
-template <> struct Shape<64> { static constexpr int QB = 1, NW = 8; };
-template <> struct Shape<128> { static constexpr int QB = 1, NW = 8; };
-template <> struct Shape<256> { static constexpr int QB = 1, NW = 4; };
+template <> struct Shape<64> { static constexpr int QB = 1, NW = 4, WPC = 2; };
+template <> struct Shape<128> { static constexpr int QB = 1, NW = 4, WPC = 2; };
+template <> struct Shape<256> { static constexpr int QB = 1, NW = 4, WPC = 1; };
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, float c,
                     uint32_t qflip, hipStream_t stream) {
-    constexpr int QB = Shape<D>::QB, NW = Shape<D>::NW;
-    constexpr int BM = Tile<D, QB, NW>::BM;
+    constexpr int QB = Shape<D>::QB, NW = Shape<D>::NW, WPC = Shape<D>::WPC;
+    constexpr int BM = Tile<D, QB, NW, WPC>::BM;
     const int ntq = (N + BM - 1) / BM;
     const long long nwg = (long long)BH * ntq;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fa_fwd16_kernel<T, D, QB, NW, CAUSAL>), dim3((unsigned)nwg), dim3(64 * NW), 0, stream,
+    hipLaunchKernelGGL((fa_fwd16_kernel<T, D, QB, NW, WPC, CAUSAL>), dim3((unsigned)nwg), dim3(64 * NW), 0, stream,
                        (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, N, BH, ntq, c, qflip);
     return hipGetLastError();
 }
