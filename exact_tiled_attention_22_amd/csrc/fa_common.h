@@ -64,6 +64,11 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base));
 }
 
+// Same copy with a wave-uniform 64-bit base (scalar registers) and a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Round-to-nearest-even packing of 8 floats into the MFMA operand of type T.

@@ -10,8 +10,8 @@
 // vector ALUs.
 //
 // Work layout (one workgroup = NW waves = BM = NW * 32 * QB query rows of one (b, h)):
-//   * each wave owns QB blocks of 32 query rows; its Q operand is loaded once (HBM -> LDS ->
-//     registers) and stays in registers;
+//   * each wave owns QB blocks of 32 query rows; its Q operand is loaded once from HBM straight into
+//     registers (together with the first K/V copies, so the prologue pays one memory latency);
 //   * key/value tiles of BN = 64 rows stream through two LDS stages each; K runs one tile ahead of V:
 //     during iteration j the LDS holds K_{j+1} and V_j while K_{j+2} and V_{j+1} are copied in, so
 //     one barrier per tile suffices;
@@ -45,15 +45,15 @@ struct Tile {
     static constexpr int Q_CHUNKS = BM * CPR;
     static constexpr int QLPT = Q_CHUNKS / THREADS;
     static constexpr int Q_BYTES = Q_CHUNKS * 16;
-    // WPC workgroups share a CU's 160 KiB of LDS.  The Q staging area gets its own region after the
-    // K/V stages when that still fits, otherwise it aliases stage 1 (K1|V1) during the prologue.
+    // WPC workgroups share a CU's 160 KiB of LDS: two K stages and two V stages.  The in-order
+    // pipeline stages Q through stage 1 (K1|V1) during its prologue; the K-ahead pipeline loads Q
+    // straight into registers.
     static constexpr int LDS_LIMIT = 160 * 1024 / WPC;
-    static constexpr bool Q_SEPARATE = Q_BYTES + 4 * KV_BYTES <= LDS_LIMIT;
-    static constexpr int LDS_BYTES = Q_SEPARATE ? Q_BYTES + 4 * KV_BYTES : 4 * KV_BYTES;
+    static constexpr int LDS_BYTES = 4 * KV_BYTES;
     static constexpr int OFF_K0 = 0, OFF_V0 = KV_BYTES, OFF_K1 = 2 * KV_BYTES, OFF_V1 = 3 * KV_BYTES;
-    static constexpr int OFF_Q = Q_SEPARATE ? 4 * KV_BYTES : OFF_K1;
+    static constexpr int OFF_Q = OFF_K1;
     static_assert(CHUNKS % THREADS == 0 && Q_CHUNKS % THREADS == 0, "tiles split evenly over threads");
-    static_assert(Q_SEPARATE || Q_BYTES <= 2 * KV_BYTES, "Q staging must fit in stage 1");
+    static_assert(Q_BYTES <= 2 * KV_BYTES, "Q staging must fit in stage 1");
     static_assert(LDS_BYTES <= LDS_LIMIT, "LDS budget");
     static_assert(LPT <= 16, "vmcnt range");
 };
@@ -83,18 +83,33 @@ struct Fwd {
     static constexpr int OFF_K0 = TL::OFF_K0, OFF_V0 = TL::OFF_V0, OFF_K1 = TL::OFF_K1, OFF_V1 = TL::OFF_V1;
     static constexpr int OFF_Q = TL::OFF_Q;
 
-    // Copy rows [r0, r0 + ROWS) of a [N, D] slice into an LDS tile (rows >= N read row N-1; they are
-    // masked or never stored).  Slot s of the tile holds chunk (s % CPR) ^ swz(row) of row s / CPR.
+    // Copy rows [r0, r0 + ROWS) of a [N, D] slice into an LDS tile, ROWS = NLOADS * THREADS / CPR.
+    // Slot s of the tile holds chunk (s % CPR) ^ swz(row) of row s / CPR.  When every row exists the
+    // copies use a scalar tile base and per-lane 32-bit offsets; a ragged last tile reads row N-1 in
+    // place of the missing rows (they are masked or never stored).
     template <int NLOADS>
     static __device__ __forceinline__ void copy_rows(const T* __restrict__ src, int r0, int N, uint32_t lds,
                                                      int tid, int wave) {
+        constexpr int ROWS = NLOADS * TL::THREADS / CPR;
+        if (r0 + ROWS <= N) {
+            const T* base = src + (size_t)r0 * D;
 #pragma unroll
-        for (int t = 0; t < NLOADS; ++t) {
-            const int slot = t * TL::THREADS + tid;
-            const int row = slot / CPR;
-            const int c = (slot % CPR) ^ swz<CPR>(row);
-            const T* g = src + (size_t)min(r0 + row, N - 1) * D + c * 8;
-            dma16(g, lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
+            for (int t = 0; t < NLOADS; ++t) {
+                const int slot = t * TL::THREADS + tid;
+                const int row = slot / CPR;
+                const int c = (slot % CPR) ^ swz<CPR>(row);
+                dma16s(base, (uint32_t)((row * D + c * 8) * (int)sizeof(T)),
+                       lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NLOADS; ++t) {
+                const int slot = t * TL::THREADS + tid;
+                const int row = slot / CPR;
+                const int c = (slot % CPR) ^ swz<CPR>(row);
+                const T* g = src + (size_t)min(r0 + row, N - 1) * D + c * 8;
+                dma16(g, lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
+            }
         }
     }
 
@@ -155,11 +170,17 @@ struct Fwd {
         bool grow = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            float mx = fmaxf(s[qb][0][0], s[qb][1][0]);
+            // 32 values -> 1 as a shallow tree of 3-input maxima (short dependency chain)
+            float t1[11];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+            for (int i = 0; i < 10; ++i) {
+                const int a = 3 * i, b = 3 * i + 1, d = 3 * i + 2;
+                t1[i] = fmaxf(fmaxf(s[qb][a >> 4][a & 15], s[qb][b >> 4][b & 15]), s[qb][d >> 4][d & 15]);
+            }
+            t1[10] = fmaxf(s[qb][1][14], s[qb][1][15]);
+            const float t2a = fmaxf(fmaxf(t1[0], t1[1]), t1[2]), t2b = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
+            const float t2c = fmaxf(fmaxf(t1[6], t1[7]), t1[8]), t2d = fmaxf(t1[9], t1[10]);
+            const float mx = fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d));
             mt[qb] = halves_max(mx) * c;
             grow |= mt[qb] > m_run[qb] + kTau;
         }
@@ -182,19 +203,21 @@ struct Fwd {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const float negm = -m_run[qb];
-            float ls = 0.0f;
+            float part[4];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 float e[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    e[r] = fast_exp2(__builtin_fmaf(s[qb][kb][r], c, negm));
-                    ls += e[r];
-                }
+                for (int r = 0; r < 16; ++r) e[r] = fast_exp2(__builtin_fmaf(s[qb][kb][r], c, negm));
                 p[qb][kb * 2 + 0] = VT::pack(e);
                 p[qb][kb * 2 + 1] = VT::pack(e + 8);
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const float* q = e + 8 * hf;
+                    part[kb * 2 + hf] = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+                }
             }
-            l_run[qb] += ls;
+            l_run[qb] += (part[0] + part[1]) + (part[2] + part[3]);
         }
     }
 
@@ -273,7 +296,6 @@ struct Fwd {
                                                    const T* __restrict__ V, T* __restrict__ O,
                                                    float* __restrict__ LSE, int N, int BH, int ntq, float c,
                                                    uint32_t qflip, char* smem) {
-        static_assert(!TL::Q_SEPARATE, "the in-order pipeline stages Q in stage 1");
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -382,35 +404,24 @@ struct Fwd {
             ln.vb = (i16 & 1) * 8;
         }
 
-        // ---- prologue: Q, K_0, V_0 (and K_1) into LDS ----
-        copy_rows<TL::QLPT>(Qh, q0, N, lbase + OFF_Q, tid, wave);
-        copy_rows<LPT>(Kh, 0, N, lbase + OFF_K0, tid, wave);
-        copy_rows<LPT>(Vh, 0, N, lbase + OFF_V0, tid, wave);
-        if constexpr (TL::Q_SEPARATE) {
-            if (nt > 1) {
-                copy_rows<LPT>(Kh, BN, N, lbase + OFF_K1, tid, wave);
-                wait_vmcnt<2 * LPT>();
-            } else {
-                wait_vmcnt<LPT>();
-            }
-        } else {
-            wait_vmcnt<LPT>();
-        }
-        lds_barrier();
-
+        // ---- prologue: Q straight into registers, K_0, V_0, K_1 into LDS, one memory latency ----
+        // Q operand (B of the score MFMA): lane supplies Q[q0w + qb*32 + n32][ks*16 + h*8 + 0..7]
         x8 qreg[QB][KS];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const int row = wave * QW + qb * 32 + n32;
-            const char* qrow = smem + OFF_Q + row * CPR * 16;
-            const int qsw = swz<CPR>(row);
+            const T* src = Qh + (size_t)min(q0w + qb * 32 + n32, N - 1) * D + h * 8;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                i32x4 raw = *(const i32x4*)(qrow + ((2 * ks + h) ^ qsw) * 16);
+                i32x4 raw = *(const i32x4*)(src + ks * 16);
                 raw ^= (int)qflip;
                 qreg[qb][ks] = __builtin_bit_cast(x8, raw);
             }
         }
+        copy_rows<LPT>(Kh, 0, N, lbase + OFF_K0, tid, wave);
+        copy_rows<LPT>(Vh, 0, N, lbase + OFF_V0, tid, wave);
+        if (nt > 1) copy_rows<LPT>(Kh, BN, N, lbase + OFF_K1, tid, wave);
+        wait_vmcnt<0>();
+        lds_barrier();
 
         f32x16 oacc[QB][CB];
         float m_run[QB], l_run[QB];
@@ -424,10 +435,6 @@ struct Fwd {
 
         f32x16 s0[QB][2], s1[QB][2];
         scores(smem + OFF_K0, qreg, s0, ln);
-        if constexpr (!TL::Q_SEPARATE) {
-            lds_barrier();  // every wave has its Q operand: stage 1 may be overwritten
-            if (nt > 1) copy_rows<LPT>(Kh, BN, N, lbase + OFF_K1, tid, wave);
-        }
 
         // ---- main loop: iteration j holds K_{j+1} and V_j, copies K_{j+2} and V_{j+1} ----
         auto iteration = [&](int j, f32x16 (&cur)[QB][2], f32x16 (&nxt)[QB][2], int okn, int ov, uint32_t dk,

@@ -73,15 +73,30 @@ struct Fwd8 {
     static constexpr int KS = D / 64;  // k-steps of the score product
     static constexpr int CB = D / 32;  // 32-column output blocks
 
+    // Copy rows [r0, r0 + ROWS) into an LDS tile (scalar base + lane offsets when every row exists;
+    // a ragged last tile reads row N-1 in place of the missing rows).
     template <int NLOADS>
     static __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, int r0, int N, uint32_t lds,
                                                      int tid, int wave) {
+        constexpr int ROWS = NLOADS * TL::THREADS / CPR;
+        if (r0 + ROWS <= N) {
+            const uint8_t* base = src + (size_t)r0 * D;
 #pragma unroll
-        for (int t = 0; t < NLOADS; ++t) {
-            const int slot = t * TL::THREADS + tid;
-            const int row = slot / CPR;
-            const int c = (slot % CPR) ^ swz8<CPR>(row);
-            dma16(src + (size_t)min(r0 + row, N - 1) * D + c * 16, lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
+            for (int t = 0; t < NLOADS; ++t) {
+                const int slot = t * TL::THREADS + tid;
+                const int row = slot / CPR;
+                const int c = (slot % CPR) ^ swz8<CPR>(row);
+                dma16s(base, (uint32_t)(row * D + c * 16), lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NLOADS; ++t) {
+                const int slot = t * TL::THREADS + tid;
+                const int row = slot / CPR;
+                const int c = (slot % CPR) ^ swz8<CPR>(row);
+                dma16(src + (size_t)min(r0 + row, N - 1) * D + c * 16,
+                      lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
+            }
         }
     }
 
