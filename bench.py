@@ -132,8 +132,9 @@ def cpu_baseline(w, seed: int, budget_s: float = 12.0):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    # the GPU needs ~40 ms of sustained load to reach its working clock: warm up well past that
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",

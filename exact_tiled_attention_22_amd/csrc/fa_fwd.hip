@@ -449,11 +449,16 @@ struct Fwd {
                 // next tile's scores (its K stage always holds valid data; on the last tile the result is
                 // unused) in the same basic block as this tile's exponentials so the two overlap; with
                 // d = 256 the registers only allow the two in sequence
+                // raised wave priority while this wave streams MFMAs: the other workgroup's wave on
+                // the SIMD (in its softmax-maximum or copy phase) then fills the issue gaps instead
+                // of competing with the matrix instructions
+                __builtin_amdgcn_s_setprio(1);
                 scores(smem + okn, qreg, nxt, ln);
                 x8 p[QB][4];
                 exps(cur, c, m_run, l_run, p);
                 pv(smem + ov, p, oacc, ln);
                 interleave();
+                __builtin_amdgcn_s_setprio(0);
             }
         };
         for (int j = 0; j < nt; j += 2) {
