@@ -10,9 +10,11 @@
 // multiply by float32(1/sqrt(d)); a division 448/amax; a multiply; the e4m3 conversion), so the codes
 // are a deterministic function of the input bits.
 //
-// HBM-bound: one workgroup per block reads the block once (each lane 16 or 32 contiguous bytes per
-// row), keeps it in registers when it fits (otherwise re-reads it, from L2), and writes the codes
-// with 8-byte stores.  Rows past N are not read or written.
+// HBM-bound.  Each lane owns 32 contiguous columns of one row (d/32 lanes per row), so the butterflies
+// with strides 1..16 stay inside the lane and the remaining one to three stages are DPP lane swaps
+// inside a quad / half-row.  A 256-thread workgroup covers 256*32/d rows per pass (64 for d = 128,
+// i.e. one whole 64-row block), loads it with 16-byte vector loads, keeps it in registers (up to two
+// passes), reduces the block maximum, and stores the codes with 16-byte stores.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -20,41 +22,103 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCachePasses = 8;  // blocks of up to 8 row-passes stay in registers
+constexpr int kEPL = 32;          // elements per lane
+constexpr int kCachePasses = 2;   // blocks of up to 2 row-passes stay in registers
 
-template <typename Tin>
-__device__ __forceinline__ void load8(const Tin* p, float* f);
+// Sign flips of the random +/-1 vector, as XOR masks on the raw input words: for lane position li and
+// 32-bit word k (elements 2k, 2k+1 of the lane's 32 columns), bit 15 flips element 2k and bit 31
+// flips element 2k+1.  A sign flip is exact, so (x * s) equals x with its sign bit toggled.
+struct SignMasks {
+    uint32_t w[8][16];
+};
+
+// Load the lane's 32 consecutive elements (optionally sign-flipped) as float32.
+template <typename Tin, bool ROT>
+__device__ __forceinline__ void load32(const Tin* p, const uint32_t* m, float* f);
 template <>
-__device__ __forceinline__ void load8<float>(const float* p, float* f) {
-    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+__device__ __forceinline__ void load32<float, false>(const float* p, const uint32_t*, float* f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { f[i] = a[i]; f[4 + i] = b[i]; }
+    for (int v = 0; v < 8; ++v) {
+        const f32x4 a = *(const f32x4*)(p + 4 * v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[4 * v + i] = a[i];
+    }
 }
 template <>
-__device__ __forceinline__ void load8<__bf16>(const __bf16* p, float* f) {
-    const bf16x8 a = *(const bf16x8*)p;
+__device__ __forceinline__ void load32<float, true>(const float* p, const uint32_t* m, float* f) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = (float)a[i];
+    for (int v = 0; v < 8; ++v) {
+        const i32x4 a = *(const i32x4*)(p + 4 * v);
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+            const uint32_t mk = m[2 * v + i / 2];
+            f[4 * v + i] = __uint_as_float((uint32_t)a[i] ^ (mk << 16));
+            f[4 * v + i + 1] = __uint_as_float((uint32_t)a[i + 1] ^ (mk & 0x80000000u));
+        }
+    }
+}
+template <bool ROT>
+__device__ __forceinline__ void load32_bf16(const __bf16* p, const uint32_t* m, float* f) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const i32x4 a = *(const i32x4*)(p + 8 * v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t wd = ROT ? ((uint32_t)a[i] ^ m[4 * v + i]) : (uint32_t)a[i];
+            f[8 * v + 2 * i] = __uint_as_float(wd << 16);
+            f[8 * v + 2 * i + 1] = __uint_as_float(wd & 0xffff0000u);
+        }
+    }
+}
+template <bool ROT>
+__device__ __forceinline__ void load32_f16(const _Float16* p, const uint32_t* m, float* f) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const i32x4 a = *(const i32x4*)(p + 8 * v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t wd = ROT ? ((uint32_t)a[i] ^ m[4 * v + i]) : (uint32_t)a[i];
+            f[8 * v + 2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xffffu));
+            f[8 * v + 2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
+        }
+    }
 }
 template <>
-__device__ __forceinline__ void load8<_Float16>(const _Float16* p, float* f) {
-    const f16x8 a = *(const f16x8*)p;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = (float)a[i];
+__device__ __forceinline__ void load32<__bf16, false>(const __bf16* p, const uint32_t* m, float* f) {
+    load32_bf16<false>(p, m, f);
+}
+template <>
+__device__ __forceinline__ void load32<__bf16, true>(const __bf16* p, const uint32_t* m, float* f) {
+    load32_bf16<true>(p, m, f);
+}
+template <>
+__device__ __forceinline__ void load32<_Float16, false>(const _Float16* p, const uint32_t* m, float* f) {
+    load32_f16<false>(p, m, f);
+}
+template <>
+__device__ __forceinline__ void load32<_Float16, true>(const _Float16* p, const uint32_t* m, float* f) {
+    load32_f16<true>(p, m, f);
 }
 
-// Rotate 8 consecutive elements of a row held by one lane; the row spans L = D/8 lanes.
+// value of lane (l ^ M) for M = 1, 2 (quad permutes).  Every source lane lies in the same quad, so
+// the zero-fill flag never applies; it lets the compiler fold the move into the add that consumes it.
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+    const int v = __float_as_int(x);
+    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));
+}
+
+// Walsh-Hadamard transform of a row whose 32-column pieces sit in consecutive lanes (this lane is
+// piece li): butterflies of strides 1..16 inside the lane, strides 32, 64, 128 across lanes, then the
+// 1/sqrt(d) factor.  Across lanes the lower piece forms other + x and the upper piece other + (-x),
+// which is the same IEEE operation as other - x.
 template <int D>
-__device__ __forceinline__ void rotate8(float* x, uint32_t sign8, int li, float rs) {
-    // sign flip (exact); bit e of sign8 = column li*8 + e is negated
+__device__ __forceinline__ void hadamard32(float* x, int li, float rs) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-        if ((sign8 >> e) & 1) x[e] = -x[e];
-    // in-lane butterflies, strides 1, 2, 4
+    for (int hs = 1; hs < kEPL; hs <<= 1) {
 #pragma unroll
-    for (int hs = 1; hs < 8; hs <<= 1) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < kEPL; ++e) {
             if ((e & hs) == 0) {
                 const float a = x[e], b = x[e + hs];
                 x[e] = a + b;
@@ -62,57 +126,86 @@ __device__ __forceinline__ void rotate8(float* x, uint32_t sign8, int li, float 
             }
         }
     }
-    // cross-lane butterflies, strides 8, 16, ..., D/2 (partner lane li ^ (stride / 8))
+    // each pass first forms all 32 operands, then all 32 DPP adds: a DPP read of a register written
+    // by the instruction just before it would cost two wait states
+    auto cross = [&](auto tag) {
+        constexpr int M = decltype(tag)::value;
+        const uint32_t neg = (li & M) ? 0x80000000u : 0u;
+        float own[kEPL];
 #pragma unroll
-    for (int ls = 1; ls < D / 8; ls <<= 1) {
-        const bool upper = (li & ls) != 0;
+        for (int e = 0; e < kEPL; ++e) own[e] = __uint_as_float(__float_as_uint(x[e]) ^ neg);
+        if constexpr (M == 4) {
+            // half-row mirror first (lane i reads 7 - i), the quad reversal is folded into the add
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float other = __shfl_xor(x[e], ls, 64);
-            x[e] = upper ? (other - x[e]) : (x[e] + other);
+            for (int e = 0; e < kEPL; ++e)
+                x[e] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[e]), 0x141, 0xF, 0xF, true));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < kEPL; ++e)
+                x[e] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[e]), 0x1B, 0xF, 0xF, true)) + own[e];
+        } else {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < kEPL; ++e) x[e] = lane_xor<M>(x[e]) + own[e];
         }
-    }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (D >= 64) cross(std::integral_constant<int, 1>{});
+    if constexpr (D >= 128) cross(std::integral_constant<int, 2>{});
+    if constexpr (D >= 256) cross(std::integral_constant<int, 4>{});
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = x[e] * rs;
+    for (int e = 0; e < kEPL; ++e) x[e] = x[e] * rs;
 }
 
 template <typename Tin, int D, bool ROT, bool CACHE>
 __global__ __launch_bounds__(kThreads) void fp8_prep_kernel(const Tin* __restrict__ X, uint8_t* __restrict__ X8,
                                                             float* __restrict__ S, int N, int block, int nblk,
-                                                            float rs, uint64_t s0, uint64_t s1, uint64_t s2,
-                                                            uint64_t s3) {
-    constexpr int L = D / 8;             // lanes per row
-    constexpr int RP = kThreads / L;     // rows per pass
+                                                            float rs, SignMasks sm) {
+    constexpr int LPR = D / kEPL;        // lanes per row
+    constexpr int RP = kThreads / LPR;   // rows per pass
     __shared__ float red[kThreads / 64];
     const int tid = threadIdx.x;
-    const int li = tid % L;              // position of this lane's 8 columns in the row
-    const uint64_t sw = li < 8 ? s0 : li < 16 ? s1 : li < 24 ? s2 : s3;
-    const uint32_t sign8 = (uint32_t)(sw >> ((li & 7) * 8)) & 0xFFu;
-    const int rsub = tid / L;            // row within a pass
+    const int li = tid % LPR;            // this lane holds columns li*32 .. li*32+31
+    uint32_t mask[16];
+    if constexpr (ROT) {
+#pragma unroll
+        for (int k = 0; k < 16; k += 4) {
+            const i32x4 t = *(const i32x4*)&sm.w[li][k];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mask[k + i] = (uint32_t)t[i];
+        }
+    }
+    const int rsub = tid / LPR;          // row within a pass
     const int bh = blockIdx.x / nblk, bi = blockIdx.x % nblk;
     const int r0 = bi * block;
     const int rows = min(block, N - r0);
     const int passes = (rows + RP - 1) / RP;
-    const size_t base = ((size_t)bh * N + r0) * D + li * 8;
+    const size_t base = ((size_t)bh * N + r0) * D + li * kEPL;
 
-    float cache[CACHE ? kCachePasses : 1][8];
+    float cache[CACHE ? kCachePasses : 1][kEPL];
     float amax = 0.0f;
-    for (int p = 0; p < (CACHE ? kCachePasses : passes); ++p) {
-        if (CACHE && p >= passes) break;
-        const int r = p * RP + rsub;
-        float x[8];
-        if (r < rows) {
-            load8<Tin>(X + base + (size_t)r * D, x);
-        } else {
+    // rows past the end of the block re-read the block's last row: the block maximum is unchanged
+    // and their codes are not stored
+    auto load_rot = [&](int p, float* x) {
+        const int r = min(p * RP + rsub, rows - 1);
+        load32<Tin, ROT>(X + base + (size_t)r * D, mask, x);
+        if (ROT) hadamard32<D>(x, li, rs);
+    };
+    if constexpr (CACHE) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+        for (int p = 0; p < kCachePasses; ++p) {
+            if (p < passes) {
+                load_rot(p, cache[p]);
+#pragma unroll
+                for (int e = 0; e < kEPL; ++e) amax = fmaxf(amax, fabsf(cache[p][e]));
+            }
         }
-        if (ROT) rotate8<D>(x, sign8, li, rs);
+    } else {
+        for (int p = 0; p < passes; ++p) {
+            float x[kEPL];
+            load_rot(p, x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
-        if (CACHE) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) cache[p][e] = x[e];
+            for (int e = 0; e < kEPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
         }
     }
     // block-wide max
@@ -129,65 +222,70 @@ __global__ __launch_bounds__(kThreads) void fp8_prep_kernel(const Tin* __restric
     const float inv = fminf(448.0f / safe, 3.402823466e38f);
     if (tid == 0) S[(size_t)bh * nblk + bi] = zero ? 1.0f : safe / 448.0f;
 
-    for (int p = 0; p < (CACHE ? kCachePasses : passes); ++p) {
-        if (CACHE && p >= passes) break;
+    auto store = [&](int p, const float* x) {
         const int r = p * RP + rsub;
-        if (r >= rows) continue;
-        float x[8];
-        if (CACHE) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = cache[p][e];
-        } else {
-            load8<Tin>(X + base + (size_t)r * D, x);
-            if (ROT) rotate8<D>(x, sign8, li, rs);
-        }
-        i32x2 packed = {0, 0};
+        if (r >= rows) return;
+        i32x4 q[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
         if (!zero) {
-            float y[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(x[e] * inv, -448.0f), 448.0f);
-            int w0 = 0, w1 = 0;
-            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], w0, false);
-            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
-            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], w1, false);
-            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
-            packed = i32x2{w0, w1};
+            for (int w = 0; w < 8; ++w) {
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(x[4 * w + e] * inv, -448.0f), 448.0f);
+                int wd = 0;
+                wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], wd, false);
+                wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], wd, true);
+                q[w >> 2][w & 3] = wd;
+            }
         }
-        *(i32x2*)(X8 + base + (size_t)r * D) = packed;
+        i32x4* dst = (i32x4*)(X8 + base + (size_t)r * D);
+        dst[0] = q[0];
+        dst[1] = q[1];
+    };
+    if constexpr (CACHE) {
+#pragma unroll
+        for (int p = 0; p < kCachePasses; ++p)
+            if (p < passes) store(p, cache[p]);
+    } else {
+        for (int p = 0; p < passes; ++p) {
+            float x[kEPL];
+            load_rot(p, x);
+            store(p, x);
+        }
     }
 }
 
 template <typename Tin, int D, bool ROT>
 hipError_t launch_prep_t(const void* x, void* x8, float* scales, int block, int BH, int N, float rs,
-                         const uint64_t* sb, hipStream_t stream) {
-    constexpr int RP = kThreads / (D / 8);
+                         const SignMasks& sm, hipStream_t stream) {
+    constexpr int RP = kThreads / (D / kEPL);
     const int nblk = (N + block - 1) / block;
     const long long nwg = (long long)BH * nblk;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
     const bool cache = (block + RP - 1) / RP <= kCachePasses;
     if (cache)
         hipLaunchKernelGGL((fp8_prep_kernel<Tin, D, ROT, true>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
-                           (const Tin*)x, (uint8_t*)x8, scales, N, block, nblk, rs, sb[0], sb[1], sb[2], sb[3]);
+                           (const Tin*)x, (uint8_t*)x8, scales, N, block, nblk, rs, sm);
     else
         hipLaunchKernelGGL((fp8_prep_kernel<Tin, D, ROT, false>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
-                           (const Tin*)x, (uint8_t*)x8, scales, N, block, nblk, rs, sb[0], sb[1], sb[2], sb[3]);
+                           (const Tin*)x, (uint8_t*)x8, scales, N, block, nblk, rs, sm);
     return hipGetLastError();
 }
 
 template <typename Tin, int D>
 hipError_t launch_prep_d(const void* x, void* x8, float* scales, bool rot, int block, int BH, int N, float rs,
-                         const uint64_t* sb, hipStream_t stream) {
-    return rot ? launch_prep_t<Tin, D, true>(x, x8, scales, block, BH, N, rs, sb, stream)
-               : launch_prep_t<Tin, D, false>(x, x8, scales, block, BH, N, rs, sb, stream);
+                         const SignMasks& sm, hipStream_t stream) {
+    return rot ? launch_prep_t<Tin, D, true>(x, x8, scales, block, BH, N, rs, sm, stream)
+               : launch_prep_t<Tin, D, false>(x, x8, scales, block, BH, N, rs, sm, stream);
 }
 
 template <typename Tin>
 hipError_t launch_prep_dt(const void* x, void* x8, float* scales, bool rot, int block, int BH, int N, int d,
-                          float rs, const uint64_t* sb, hipStream_t stream) {
+                          float rs, const SignMasks& sm, hipStream_t stream) {
     switch (d) {
-        case 64: return launch_prep_d<Tin, 64>(x, x8, scales, rot, block, BH, N, rs, sb, stream);
-        case 128: return launch_prep_d<Tin, 128>(x, x8, scales, rot, block, BH, N, rs, sb, stream);
-        case 256: return launch_prep_d<Tin, 256>(x, x8, scales, rot, block, BH, N, rs, sb, stream);
+        case 64: return launch_prep_d<Tin, 64>(x, x8, scales, rot, block, BH, N, rs, sm, stream);
+        case 128: return launch_prep_d<Tin, 128>(x, x8, scales, rot, block, BH, N, rs, sm, stream);
+        case 256: return launch_prep_d<Tin, 256>(x, x8, scales, rot, block, BH, N, rs, sm, stream);
         default: return hipErrorNotSupported;
     }
 }
@@ -198,10 +296,17 @@ hipError_t launch_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, 
                            const uint64_t sign_bits[4], int block, int BH, int N, int d, hipStream_t stream) {
     // float32 value of 1/sqrt(d): the double quotient rounded once to float
     const float rs = (float)(1.0 / __builtin_sqrt((double)d));
+    SignMasks sm{};
+    for (int t = 0; t < 256; ++t) {
+        if ((sign_bits[t >> 6] >> (t & 63)) & 1) {
+            const int li = t / kEPL, e = t % kEPL;
+            sm.w[li][e >> 1] |= (e & 1) ? 0x80000000u : 0x00008000u;
+        }
+    }
     switch (x_dtype) {
-        case 0: return launch_prep_dt<float>(x, x8, scales, rotate, block, BH, N, d, rs, sign_bits, stream);
-        case 1: return launch_prep_dt<_Float16>(x, x8, scales, rotate, block, BH, N, d, rs, sign_bits, stream);
-        case 2: return launch_prep_dt<__bf16>(x, x8, scales, rotate, block, BH, N, d, rs, sign_bits, stream);
+        case 0: return launch_prep_dt<float>(x, x8, scales, rotate, block, BH, N, d, rs, sm, stream);
+        case 1: return launch_prep_dt<_Float16>(x, x8, scales, rotate, block, BH, N, d, rs, sm, stream);
+        case 2: return launch_prep_dt<__bf16>(x, x8, scales, rotate, block, BH, N, d, rs, sm, stream);
         default: return hipErrorNotSupported;
     }
 }
