@@ -27,25 +27,29 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["fa_fwd.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_fp8_prep.hip", "fa_common.h"]
+# sources of the kernels each workload launches (a counter record is valid while these are unchanged)
+KERNEL_SOURCES = {
+    "bf16": ["fa_fwd.hip", "fa_common.h"], "f16": ["fa_fwd.hip", "fa_common.h"],
+    "f32": ["fa_fwd_f32.hip", "fa_common.h"], "fp8": ["fa_fwd_fp8.hip", "fa_fp8_prep.hip", "fa_common.h"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(dtype: str = "bf16") -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[dtype]:
         with open(os.path.join(ROOT, "exact_tiled_attention_22_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(cfg_id: int):
+def load_traffic(cfg_id: int, dtype: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches the sources."""
     path = os.path.join(PROFILES, f"traffic_cfg{cfg_id}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(dtype):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -80,7 +84,9 @@ def ingest_counters(cfg_id: int, fetch_csv: str, write_csv: str) -> int:
         factor = (COPY_BYTES / 1024.0) / copy_kib
         out[counter] = {"attention_kib_per_dispatch": attn_kib, "copy_kib_per_dispatch": copy_kib,
                         "copy_scale_factor": factor, "bytes_per_launch": attn_kib * 1024.0 * factor}
-    rec = {"config": cfg_id, "kernel_source_sha256_16": kernel_source_hash(),
+    from synth import CONFIGS
+
+    rec = {"config": cfg_id, "kernel_source_sha256_16": kernel_source_hash(CONFIGS[cfg_id].dtype),
            "counters": out,
            "hbm_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]}
     os.makedirs(PROFILES, exist_ok=True)
@@ -201,7 +207,7 @@ def main() -> int:
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = load_traffic(w.cfg_id)
+    traffic = load_traffic(w.cfg_id, w.dtype)
     line = {
         "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, /2 causal) and % of MI355X MFMA peak",
         "value": round(value, 2),
