@@ -11,18 +11,22 @@ What it computes, in float64 on the CPU, straight from the definitions:
   The pages say the tiled method returns the same output as this plain softmax formula
   (FlashAttention 2 + 3 — speicherbewusste Attention-Kernels, "Kernpunkte" and "Worum es geht";
   Flash Attention glossary, "/01 Was ist Flash Attention?").
+* ``attention_bwd_ref`` / ``attention_bwd_rows`` — the gradients dQ, dK, dV of that definition for a
+  given output gradient dO (the pages name the backward pass but do not write it out; the derivative
+  of the definition is the plain result the kernels must reproduce).
 * ``fp8`` — the OCP e4m3 codec, the Sylvester Walsh-Hadamard transform and the per-block absmax
   quantisation of the FP8 path (FlashAttention-3 article, "Drei technische Hebel", item 3
   "FP8-Blockquantisierung"; concept card, "Kernpunkte", FP8 with absmax scaling).
 
 Pins (tests marked ``not gpu``): brute force with ``math.fsum`` on tiny inputs, torch's float64
 CPU scaled_dot_product_attention and scipy's logsumexp/hadamard as independent library routines,
+central finite differences and torch autograd for the gradients,
 closed forms (Q = 0, constant V, causal row 0, two keys), invariances (joint key/value permutation,
 per-row score shift), and torch's float8_e4m3fn conversion for the codec.  No function here is
 "parity unpinned".
 """
 
-from .attention import attention_ref, attention_rows  # noqa: F401
+from .attention import attention_bwd_ref, attention_bwd_rows, attention_ref, attention_rows  # noqa: F401
 from .fp8 import (  # noqa: F401
     E4M3_MAX,
     dequantize_blocks,

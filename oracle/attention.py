@@ -71,3 +71,46 @@ def attention_ref(q, k, v, causal: bool, scale: float, row_chunk: int = 1024):
             o[idx][r0:r0 + len(rows)] = o_c
             lse[idx][r0:r0 + len(rows)] = lse_c
     return o, lse
+
+
+def attention_bwd_rows(qh, kh, vh, doh, causal: bool, scale: float):
+    """Gradients of the attention definition for ONE head: returns (dQ, dK, dV) float64 [N, d].
+
+    The pages name the backward pass (FlashAttention 2 + 3 — speicherbewusste Attention-Kernels,
+    "Kernpunkte": FlashAttention 2 parallelises it better) but do not write it out; this is the
+    derivative of the definition above, for a loss L whose gradient with respect to O is dO:
+
+        P_ij  = exp(s_ij - lse_i) on visible keys, 0 elsewhere      (the softmax of each row)
+        dV    = P^T dO
+        dP    = dO V^T
+        D_i   = sum_t dO[i,t] O[i,t]          (= sum_j P_ij dP_ij, the row term of the softmax)
+        dS_ij = P_ij (dP_ij - D_i)             (softmax derivative, row by row)
+        dQ    = scale dS K,   dK = scale dS^T Q
+
+    Full score rows, float64, no tiling.
+    """
+    qh, kh, vh, doh = _f64(qh), _f64(kh), _f64(vh), _f64(doh)
+    n = qh.shape[0]
+    s = float(scale) * (qh @ kh.T)
+    if causal:
+        s = np.where(np.arange(n)[None, :] <= np.arange(n)[:, None], s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    o = p @ vh
+    dv = p.T @ doh
+    dp = doh @ vh.T
+    dd = (doh * o).sum(axis=1, keepdims=True)
+    ds = p * (dp - dd)
+    dq = float(scale) * (ds @ kh)
+    dk = float(scale) * (ds.T @ qh)
+    return dq, dk, dv
+
+
+def attention_bwd_ref(q, k, v, do, causal: bool, scale: float):
+    """attention_bwd_rows over leading (batch, head) dims; tensors [..., N, d]."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    dq, dk, dv = (np.empty_like(q), np.empty_like(k), np.empty_like(v))
+    for idx in np.ndindex(*q.shape[:-2]):
+        dq[idx], dk[idx], dv[idx] = attention_bwd_rows(q[idx], k[idx], v[idx], do[idx], causal, scale)
+    return dq, dk, dv
