@@ -1,4 +1,4 @@
-"""Exact tiled attention forward for AMD Instinct MI355X (gfx950).
+"""Exact tiled attention (forward and backward) for AMD Instinct MI355X (gfx950).
 
 The compute lives in ``libfa.so`` (hand-written HIP kernels behind the C ABI of ``include/fa.h``);
 this package only loads it and marshals arguments.
@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     FA_FP8_E4M3,
     FaError,
     abi_version,
+    bwd,
     fp8_prep,
     fwd,
     last_error,

@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd.restype = i
     L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, ctypes.POINTER(_Fp8Scales), vp]
     L.fa_fwd_ex.restype = i
+    L.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
+    L.fa_bwd.restype = i
     L.fa_fp8_prep.argtypes = [vp, i, vp, vp, vp, i, i, i, i, vp]
     L.fa_fp8_prep.restype = i
     L.fa_status_str.argtypes = [i]
@@ -133,6 +135,31 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
     del keep
     _check(st, "fa_fwd_ex")
     return out, (lse if return_lse else None)
+
+
+def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = None, dq=None, dk=None, dv=None,
+        delta=None):
+    """Attention backward through fa_bwd: gradients (dq, dk, dv) of fwd's output for the output
+    gradient ``dout``; ``o`` and ``lse`` are fwd's results for the same call.  float16/bfloat16, d in
+    {64, 128}.  ``delta`` is the float32 [B, H, N] workspace (allocated when not given)."""
+    _check_qkv(q, k, v)
+    for t in (o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("o and dout must match q in shape, dtype and device, contiguous")
+    B, H, N, d = q.shape
+    if lse is None or lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                      _ptr(delta), B, H, N, d, int(bool(causal)), float(scale), DTYPE_CODE[q.dtype],
+                      _stream(q.device))
+    _check(st, "fa_bwd")
+    return dq, dk, dv
 
 
 def fp8_prep(x, signs=None, block: int = 64, out=None, scales=None):

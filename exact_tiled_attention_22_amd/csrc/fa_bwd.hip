@@ -1,0 +1,450 @@
+// fa_bwd.hip — attention backward (dQ, dK, dV) for 16-bit floats on gfx950.
+//
+// The pages name the backward pass ("FlashAttention 2 + 3 — speicherbewusste Attention-Kernels",
+// "Kernpunkte": FlashAttention 2 gains from better parallelism in it) without writing it out.  What
+// is computed is the derivative of the attention definition for a given output gradient dO, using
+// the row log-sum-exp saved by the forward pass:
+//     P = exp(scale Q K^T - lse)   (visible keys),   D_i = sum_t dO[i,t] O[i,t],
+//     dS = P o (dO V^T - D),   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
+// Like the forward pass it never stores an N x N matrix: P and dS are rebuilt tile by tile from Q,
+// K and lse.  Three launches, no atomics (the result is deterministic):
+//   1. delta_kernel: D = rowsum(dO o O), float32 [B,H,N] in a caller-provided buffer;
+//   2. BwdQ: one workgroup per 128 query rows streams the K/V tiles (as the forward pass does) and
+//      accumulates dQ^T = K^T dS^T in registers;
+//   3. BwdKV: one workgroup per 128 keys streams the Q/dO tiles (with their lse and D) and
+//      accumulates dV^T = dO^T P and dK^T = Q^T dS in registers.
+// Operand conventions are the forward pass's: v_mfma_f32_32x32x16 with the A-operand rows permuted
+// so that 8 consecutive accumulator registers of a lane hold 8 consecutive rows (keys in BwdQ,
+// queries in BwdKV), which lets P and dS feed the next MFMA as its B operand in place, and
+// transposed operands (K^T, dO^T, Q^T) read from LDS with ds_read_b64_tr_b16.
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 16-byte-chunk XOR swizzle of an LDS row (the forward pass's, for the same two access patterns:
+// a 16-row operand fetch of one chunk and a transposing fetch of 4 chunks x 4 rows).
+template <int CPR>
+__device__ __forceinline__ int bswz(int row) {
+    if constexpr (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// Copy rows [r0, r0 + ROWS) of a [N, D] slice (2-byte elements) into an LDS tile with THREADS
+// threads; rows past N repeat row N-1 (they are masked).  Slot s holds chunk (s % CPR) ^ swz(row).
+template <typename T, int D, int ROWS, int THREADS>
+__device__ __forceinline__ void copy_tile(const T* __restrict__ src, int r0, int N, uint32_t lds, int tid,
+                                          int wave) {
+    constexpr int CPR = D / 8, NL = ROWS * CPR / THREADS;
+    static_assert(ROWS * CPR % THREADS == 0, "tile splits evenly");
+    if (r0 + ROWS <= N) {
+        const T* base = src + (size_t)r0 * D;
+#pragma unroll
+        for (int t = 0; t < NL; ++t) {
+            const int slot = t * THREADS + tid;
+            const int row = slot / CPR;
+            const int c = (slot % CPR) ^ bswz<CPR>(row);
+            dma16s(base, (uint32_t)((row * D + c * 8) * (int)sizeof(T)),
+                   lds + (uint32_t)((t * THREADS + wave * 64) * 16));
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < NL; ++t) {
+            const int slot = t * THREADS + tid;
+            const int row = slot / CPR;
+            const int c = (slot % CPR) ^ bswz<CPR>(row);
+            dma16(src + (size_t)min(r0 + row, N - 1) * D + c * 8, lds + (uint32_t)((t * THREADS + wave * 64) * 16));
+        }
+    }
+}
+
+// Per-lane fetch geometry inside an LDS tile of 64 rows (lane = 32 h + n32).
+template <int CPR>
+struct Geo {
+    int prow, h;        // A operand: permuted row prow (+32 for the second block), chunk 2*ks + h
+    int trow, tcc, tb;  // transposing read: row u*4 + trow, chunk cb*4 + tcc, byte tb
+    __device__ __forceinline__ Geo(int lane) {
+        const int n32 = lane & 31;
+        h = lane >> 5;
+        prow = ((n32 >> 4) & 1) * 16 + ((n32 >> 2) & 1) * 8 + ((n32 >> 3) & 1) * 4 + (n32 & 3);
+        const int i16 = lane & 15, G = lane >> 4;
+        trow = (G >> 1) * 8 + (i16 >> 2);
+        tcc = (G & 1) * 2 + ((i16 & 3) >> 1);
+        tb = (i16 & 1) * 8;
+    }
+    // A operand for k-step ks of row block rb
+    __device__ __forceinline__ int aoff(int rb, int ks) const {
+        const int row = rb * 32 + prow;
+        return (row * CPR + ((2 * ks + h) ^ bswz<CPR>(row))) * 16;
+    }
+    // transposed operand (rows = d block cb, contraction = 16 tile rows from 16 * st), half u
+    __device__ __forceinline__ int toff(int cb, int st, int u) const {
+        const int row = st * 16 + u * 4 + trow;
+        return (row * CPR + ((cb * 4 + tcc) ^ bswz<CPR>(row))) * 16 + tb;
+    }
+};
+
+// ---------------------------------------------------------------------------------------------
+// D = rowsum(dO o O) in float32: D/8 lanes per row, 16-byte loads, a butterfly sum over the row's lanes.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ O, const T* __restrict__ dO,
+                                                    float* __restrict__ Dl, long long rows) {
+    using x8 = typename Vec<T>::x8;
+    constexpr int LPR = D / 8, RPB = 256 / LPR;
+    const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int li = threadIdx.x % LPR;
+    float acc = 0.0f;
+    if (row < rows) {
+        const x8 o = *(const x8*)(O + row * D + li * 8);
+        const x8 g = *(const x8*)(dO + row * D + li * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
+    }
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (li == 0 && row < rows) Dl[row] = acc;
+}
+
+// ---------------------------------------------------------------------------------------------
+// dQ: one workgroup = 4 waves x 32 query rows; key/value tiles of 64 rows through two LDS stages.
+template <typename T, int D, bool CAUSAL>
+struct BwdQ {
+    using VT = Vec<T>;
+    using x8 = typename VT::x8;
+    using x4 = typename VT::x4;
+    static constexpr int NW = 4, THREADS = 256, QW = 32, BM = NW * QW, BN = 64;
+    static constexpr int CPR = D / 8, KS = D / 16, CB = D / 32;
+    static constexpr int TILE = BN * CPR * 16;
+    static constexpr int LDS_BYTES = 4 * TILE;  // K0 | V0 | K1 | V1
+
+    static __device__ __forceinline__ void run(const T* __restrict__ Q, const T* __restrict__ K,
+                                               const T* __restrict__ V, const T* __restrict__ dO,
+                                               const float* __restrict__ LSE, const float* __restrict__ Dl,
+                                               T* __restrict__ dQ, int N, int BH, int ntq, float c, float scale,
+                                               char* smem) {
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int n32 = lane & 31, h = lane >> 5;
+        const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+        int bh, qt;
+        map_block(blockIdx.x, BH, ntq, CAUSAL, bh, qt);
+        const size_t head = (size_t)bh * N * D;
+        const int q0 = qt * BM, q0w = q0 + wave * QW, query = q0w + n32, qrow = min(query, N - 1);
+        const int nt = ((CAUSAL ? min(N, q0 + BM) : N) + BN - 1) / BN;
+        const int ntw = ((CAUSAL ? min(N, q0w + QW) : N) + BN - 1) / BN;
+        const Geo<CPR> g(lane);
+
+        // B operands of S^T = K Q^T and dP^T = V dO^T: this lane's query row, 8 columns per k-step
+        x8 qreg[KS], dreg[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qreg[ks] = *(const x8*)(Q + head + (size_t)qrow * D + ks * 16 + h * 8);
+            dreg[ks] = *(const x8*)(dO + head + (size_t)qrow * D + ks * 16 + h * 8);
+        }
+        const float lse2 = LSE[(size_t)bh * N + qrow] * kLog2e;
+        const float dd = Dl[(size_t)bh * N + qrow];
+        copy_tile<T, D, BN, THREADS>(K + head, 0, N, lbase, tid, wave);
+        copy_tile<T, D, BN, THREADS>(V + head, 0, N, lbase + TILE, tid, wave);
+
+        f32x16 acc[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16{};
+
+        auto iteration = [&](int j, int ok, int ov, uint32_t dk, uint32_t dv) {
+            wait_vmcnt<0>();
+            lds_barrier();
+            if (j + 1 < nt) {
+                copy_tile<T, D, BN, THREADS>(K + head, (j + 1) * BN, N, lbase + dk, tid, wave);
+                copy_tile<T, D, BN, THREADS>(V + head, (j + 1) * BN, N, lbase + dv, tid, wave);
+            }
+            if (j >= ntw) return;
+            const char* kl = smem + ok;
+            const char* vl = smem + ov;
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) s[kb] = dp[kb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    s[kb] = VT::mfma(*(const x8*)(kl + g.aoff(kb, ks)), qreg[ks], s[kb]);
+                    dp[kb] = VT::mfma(*(const x8*)(vl + g.aoff(kb, ks)), dreg[ks], dp[kb]);
+                }
+            }
+            // dS^T = P^T o (dP^T - D): register r of key block kb holds key kb*32 + (r/8)*16 + h*8 + r%8
+            x8 ds[4];
+            const bool edge = (j * BN + BN > N) || (CAUSAL && j * BN + BN - 1 > q0w);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    float v8[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int r = hf * 8 + e;
+                        float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
+                        if (edge) {
+                            const int key = j * BN + kb * 32 + hf * 16 + h * 8 + e;
+                            if (key >= N || (CAUSAL && key > query)) p = 0.0f;
+                        }
+                        v8[e] = p * (dp[kb][r] - dd);
+                    }
+                    ds[kb * 2 + hf] = VT::pack(v8);
+                }
+            }
+            // dQ^T += K^T dS^T over the tile's four 16-key steps
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const x4 lo = VT::read_tr(kl + g.toff(cb, st, 0));
+                    const x4 hi = VT::read_tr(kl + g.toff(cb, st, 1));
+                    acc[cb] = VT::mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), ds[st], acc[cb]);
+                }
+            }
+        };
+        for (int j = 0; j < nt; j += 2) {
+            iteration(j, 0, TILE, 2 * TILE, 3 * TILE);
+            if (j + 1 < nt) iteration(j + 1, 2 * TILE, 3 * TILE, 0, TILE);
+        }
+        if (query < N) {
+            T* row = dQ + head + (size_t)query * D;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    x4 out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = (T)(acc[cb][gq * 4 + e] * scale);
+                    *(x4*)(row + cb * 32 + gq * 8 + h * 4) = out;
+                }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------------------------
+// dK, dV: one workgroup = 4 waves x 32 keys; query tiles of 64 rows (Q, dO, lse, D) through two
+// LDS stages.  Per stage: Q tile | dO tile | lse * log2(e) [64] | D [64].
+template <typename T, int D, bool CAUSAL>
+struct BwdKV {
+    using VT = Vec<T>;
+    using x8 = typename VT::x8;
+    using x4 = typename VT::x4;
+    static constexpr int NW = 4, THREADS = 256, KW = 32, BK = NW * KW, BQ = 64;
+    static constexpr int CPR = D / 8, KS = D / 16, CB = D / 32;
+    static constexpr int TILE = BQ * CPR * 16;
+    static constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
+    static constexpr int LDS_BYTES = 2 * STAGE;
+
+    static __device__ __forceinline__ void run(const T* __restrict__ Q, const T* __restrict__ K,
+                                               const T* __restrict__ V, const T* __restrict__ dO,
+                                               const float* __restrict__ LSE, const float* __restrict__ Dl,
+                                               T* __restrict__ dK, T* __restrict__ dV, int N, int BH, int nkt,
+                                               float c, float scale, char* smem) {
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int n32 = lane & 31, h = lane >> 5;
+        const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+        int bh, t;
+        map_block(blockIdx.x, BH, nkt, CAUSAL, bh, t);
+        const int kt = CAUSAL ? nkt - 1 - t : t;  // causal: the first key tiles see the most queries
+        const size_t head = (size_t)bh * N * D;
+        const float* lseh = LSE + (size_t)bh * N;
+        const float* dlh = Dl + (size_t)bh * N;
+        const int k0 = kt * BK, kw0 = k0 + wave * KW, key = kw0 + n32, krow = min(key, N - 1);
+        const int ntq = (N + BQ - 1) / BQ;
+        const int t0 = CAUSAL ? k0 / BQ : 0;        // first query tile with a visible key of the workgroup
+        const int t0w = CAUSAL ? kw0 / BQ : 0;      // ... of this wave
+        const Geo<CPR> g(lane);
+
+        // B operands of S = Q K^T and dP = dO V^T: this lane's key row, 8 columns per k-step
+        x8 kreg[KS], vreg[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            kreg[ks] = *(const x8*)(K + head + (size_t)krow * D + ks * 16 + h * 8);
+            vreg[ks] = *(const x8*)(V + head + (size_t)krow * D + ks * 16 + h * 8);
+        }
+        // lse and D of a query tile: wave 0 loads lse, wave 1 loads D, one row per lane (clamped)
+        auto load_ld = [&](int tq) -> float {
+            const int r = min(tq * BQ + lane, N - 1);
+            return wave == 0 ? lseh[r] * kLog2e : dlh[r];
+        };
+        auto issue = [&](int tq, uint32_t st) {
+            copy_tile<T, D, BQ, THREADS>(Q + head, tq * BQ, N, lbase + st, tid, wave);
+            copy_tile<T, D, BQ, THREADS>(dO + head, tq * BQ, N, lbase + st + TILE, tid, wave);
+        };
+        float ldv = 0.0f;
+        if (t0 < ntq) {
+            issue(t0, 0);
+            if (wave < 2) ldv = load_ld(t0);
+        }
+
+        f32x16 adk[CB], adv[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) adk[cb] = adv[cb] = f32x16{};
+
+        auto iteration = [&](int tq, uint32_t cur, uint32_t nxt) {
+            wait_vmcnt<0>();
+            if (wave < 2) *(float*)(smem + cur + 2 * TILE + wave * BQ * 4 + lane * 4) = ldv;
+            lds_barrier();
+            if (tq + 1 < ntq) {
+                issue(tq + 1, nxt);
+                if (wave < 2) ldv = load_ld(tq + 1);
+            }
+            if (tq < t0w) return;
+            const char* ql = smem + cur;
+            const char* gl = smem + cur + TILE;
+            const float* lsl = (const float*)(smem + cur + 2 * TILE);
+            const float* dsl = lsl + BQ;
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) s[qb] = dp[qb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    s[qb] = VT::mfma(*(const x8*)(ql + g.aoff(qb, ks)), kreg[ks], s[qb]);
+                    dp[qb] = VT::mfma(*(const x8*)(gl + g.aoff(qb, ks)), vreg[ks], dp[qb]);
+                }
+            }
+            // register r of query block qb holds query qb*32 + (r/8)*16 + h*8 + r%8 (of the tile)
+            x8 pb[4], dsb[4];
+            const bool edge = (tq * BQ + BQ > N) || (CAUSAL && kw0 + KW - 1 > tq * BQ);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int qb = st >> 1, hf = st & 1;
+                const int qi = qb * 32 + hf * 16 + h * 8;  // first of the 8 queries
+                const f32x4 l0 = *(const f32x4*)(lsl + qi), l1 = *(const f32x4*)(lsl + qi + 4);
+                const f32x4 d0 = *(const f32x4*)(dsl + qi), d1 = *(const f32x4*)(dsl + qi + 4);
+                float pv[8], dv8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r = hf * 8 + e;
+                    const float l2 = e < 4 ? l0[e] : l1[e - 4];
+                    const float de = e < 4 ? d0[e] : d1[e - 4];
+                    float p = fast_exp2(__builtin_fmaf(s[qb][r], c, -l2));
+                    if (edge) {
+                        const int qq = tq * BQ + qi + e;
+                        if (qq >= N || (CAUSAL && key > qq)) p = 0.0f;
+                    }
+                    pv[e] = p;
+                    dv8[e] = p * (dp[qb][r] - de);
+                }
+                pb[st] = VT::pack(pv);
+                dsb[st] = VT::pack(dv8);
+            }
+            // dV^T += dO^T P, dK^T += Q^T dS over the tile's four 16-query steps
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const x4 glo = VT::read_tr(gl + g.toff(cb, st, 0));
+                    const x4 ghi = VT::read_tr(gl + g.toff(cb, st, 1));
+                    adv[cb] = VT::mfma(__builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7), pb[st], adv[cb]);
+                    const x4 qlo = VT::read_tr(ql + g.toff(cb, st, 0));
+                    const x4 qhi = VT::read_tr(ql + g.toff(cb, st, 1));
+                    adk[cb] = VT::mfma(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), dsb[st], adk[cb]);
+                }
+            }
+        };
+        for (int tq = t0; tq < ntq; tq += 2) {
+            iteration(tq, 0, STAGE);
+            if (tq + 1 < ntq) iteration(tq + 1, STAGE, 0);
+        }
+        if (key < N) {
+            T* krw = dK + head + (size_t)key * D;
+            T* vrw = dV + head + (size_t)key * D;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    x4 ok, ov;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        ok[e] = (T)(adk[cb][gq * 4 + e] * scale);
+                        ov[e] = (T)adv[cb][gq * 4 + e];
+                    }
+                    *(x4*)(krw + cb * 32 + gq * 8 + h * 4) = ok;
+                    *(x4*)(vrw + cb * 32 + gq * 8 + h * 4) = ov;
+                }
+        }
+    }
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                       const T* __restrict__ V, const T* __restrict__ dO,
+                                                       const float* __restrict__ LSE, const float* __restrict__ Dl,
+                                                       T* __restrict__ dQ, int N, int BH, int ntq, float c,
+                                                       float scale) {
+    __shared__ __attribute__((aligned(1024))) char smem[BwdQ<T, D, CAUSAL>::LDS_BYTES];
+    BwdQ<T, D, CAUSAL>::run(Q, K, V, dO, LSE, Dl, dQ, N, BH, ntq, c, scale, smem);
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                        const T* __restrict__ V, const T* __restrict__ dO,
+                                                        const float* __restrict__ LSE, const float* __restrict__ Dl,
+                                                        T* __restrict__ dK, T* __restrict__ dV, int N, int BH,
+                                                        int nkt, float c, float scale) {
+    __shared__ __attribute__((aligned(1024))) char smem[BwdKV<T, D, CAUSAL>::LDS_BYTES];
+    BwdKV<T, D, CAUSAL>::run(Q, K, V, dO, LSE, Dl, dK, dV, N, BH, nkt, c, scale, smem);
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int N, float scale,
+                        hipStream_t stream) {
+    const long long rows = (long long)BH * N;
+    constexpr int RPB = 256 / (D / 8);
+    const long long nd = (rows + RPB - 1) / RPB;
+    const int ntq = (N + BwdQ<T, D, CAUSAL>::BM - 1) / BwdQ<T, D, CAUSAL>::BM;
+    const int nkt = (N + BwdKV<T, D, CAUSAL>::BK - 1) / BwdKV<T, D, CAUSAL>::BK;
+    if (nd > 0x7fffffffLL || (long long)BH * ntq > 0x7fffffffLL || (long long)BH * nkt > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    const float c = scale * kLog2e;
+    hipLaunchKernelGGL((delta_kernel<T, D>), dim3((unsigned)nd), dim3(256), 0, stream, (const T*)o, (const T*)dout,
+                       delta, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_q_kernel<T, D, CAUSAL>), dim3((unsigned)(BH * ntq)), dim3(256), 0, stream, (const T*)q,
+                       (const T*)k, (const T*)v, (const T*)dout, lse, (const float*)delta, (T*)dq, N, BH, ntq, c,
+                       scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_kv_kernel<T, D, CAUSAL>), dim3((unsigned)(BH * nkt)), dim3(256), 0, stream, (const T*)q,
+                       (const T*)k, (const T*)v, (const T*)dout, lse, (const float*)delta, (T*)dk, (T*)dv, N, BH,
+                       nkt, c, scale);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bwd_dt(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int N, int d,
+                         bool causal, float scale, hipStream_t stream) {
+    switch (d) {
+        case 64:
+            return causal ? launch_bwd_t<T, 64, true>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, stream)
+                          : launch_bwd_t<T, 64, false>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, stream);
+        case 128:
+            return causal ? launch_bwd_t<T, 128, true>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, stream)
+                          : launch_bwd_t<T, 128, false>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, stream);
+        default:
+            return hipErrorNotSupported;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_16(bool is_bf16, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int N, int d,
+                         bool causal, float scale, hipStream_t stream) {
+    return is_bf16 ? launch_bwd_dt<__bf16>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, d, causal, scale, stream)
+                   : launch_bwd_dt<_Float16>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, d, causal, scale,
+                                             stream);
+}
+
+}  // namespace fa

@@ -148,6 +148,45 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, nullptr, stream);
 }
 
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, float* delta, int B, int H, int N, int d, int causal, float scale, int dtype,
+           void* stream) {
+    g_err[0] = '\0';
+    if (dtype != FA_F16 && dtype != FA_BF16) {
+        if (elem_bytes(dtype) == 0) return fail(FA_ERR_DTYPE, "dtype code %d is not a fa_dtype", dtype);
+        return fail(FA_ERR_UNSUPPORTED, "fa_bwd dtype %d (supported: FA_F16, FA_BF16)", dtype);
+    }
+    if (B < 0 || H < 0 || N < 0) return fail(FA_ERR_SHAPE, "negative size B=%d H=%d N=%d", B, H, N);
+    if (causal != 0 && causal != 1) return fail(FA_ERR_ARG, "causal must be 0 or 1, got %d", causal);
+    if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale must be finite");
+    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "fa_bwd head dimension d=%d (supported: 64, 128)", d);
+    const long long BH = static_cast<long long>(B) * H;
+    if (BH == 0 || N == 0) return FA_OK;
+    if (int st = check_sizes(BH, N, d)) return st;
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta)
+        return fail(FA_ERR_NULL, "q, k, v, o, lse, dout, dq, dk, dv and delta must be non-NULL");
+    const void* all[] = {q, k, v, o, lse, dout, dq, dk, dv, delta};
+    for (const void* ptr : all)
+        if (misaligned(ptr)) return fail(FA_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    const size_t tb = static_cast<size_t>(BH) * N * d * 2, rb = static_cast<size_t>(BH) * N * 4;
+    const void* ins[] = {q, k, v, o, dout};
+    void* outs[] = {dq, dk, dv};
+    for (void* out : outs) {
+        for (const void* in : ins)
+            if (overlaps(out, tb, in, tb)) return fail(FA_ERR_ARG, "dq, dk, dv must not overlap q, k, v, o or dout");
+        if (overlaps(out, tb, lse, rb) || overlaps(out, tb, delta, rb))
+            return fail(FA_ERR_ARG, "dq, dk, dv must not overlap lse or delta");
+    }
+    if (overlaps(dq, tb, dk, tb) || overlaps(dq, tb, dv, tb) || overlaps(dk, tb, dv, tb))
+        return fail(FA_ERR_ARG, "dq, dk and dv must not overlap each other");
+    for (const void* in : ins)
+        if (overlaps(delta, rb, in, tb)) return fail(FA_ERR_ARG, "delta must not overlap the inputs");
+    if (overlaps(delta, rb, lse, rb)) return fail(FA_ERR_ARG, "delta must not overlap lse");
+    return from_hip(fa::launch_bwd_16(dtype == FA_BF16, q, k, v, o, lse, dout, dq, dk, dv, delta, static_cast<int>(BH),
+                                      N, d, causal != 0, scale, reinterpret_cast<hipStream_t>(stream)),
+                    dtype == FA_BF16 ? "fa_bwd(bf16)" : "fa_bwd(f16)");
+}
+
 int fa_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, const int8_t* hadamard, int block, int BH, int N,
                 int d, void* stream) {
     g_err[0] = '\0';

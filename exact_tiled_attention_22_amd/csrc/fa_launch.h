@@ -29,4 +29,9 @@ hipError_t launch_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, 
                            const uint64_t sign_bits[4], int block, int BH, int N, int d,
                            hipStream_t stream);
 
+// backward (bf16 / fp16, d in {64, 128}): delta <- rowsum(dout o o), then dq, then dk and dv.
+hipError_t launch_bwd_16(bool is_bf16, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int N, int d,
+                         bool causal, float scale, hipStream_t stream);
+
 }  // namespace fa

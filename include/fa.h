@@ -113,6 +113,29 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fp8_prep(const void* x, int x_dtype, void* x8, float* scales,
                 const int8_t* hadamard, int block, int BH, int N, int d, void* stream);
 
+/*
+ * Attention backward: the gradients of fa_fwd's output with respect to q, k and v for a given output
+ * gradient dout, rebuilt tile by tile from the saved row log-sum-exp (no N x N matrix in memory).
+ * The pages name the backward pass without writing it out ("FlashAttention 2 + 3 — speicherbewusste
+ * Attention-Kernels", "Kernpunkte": FlashAttention 2 improves its parallelism); what is computed is
+ * the derivative of the forward definition:
+ *     P = exp(scale q k^T - lse) on the visible keys,  D_i = sum_t dout[i,t] o[i,t],
+ *     dS = P o (dout v^T - D),  dq = scale dS k,  dk = scale dS^T q,  dv = P^T dout.
+ *   q, k, v, o, dout : DEVICE [B,H,N,d] inputs of type `dtype` (FA_F16 or FA_BF16); o is fa_fwd's
+ *                      output for the same q, k, v, causal, scale.
+ *   lse              : DEVICE [B,H,N] float32, fa_fwd's lse for the same call (required).
+ *   dq, dk, dv       : DEVICE [B,H,N,d] outputs of type `dtype`; must overlap neither each other nor
+ *                      any input.
+ *   delta            : DEVICE [B,H,N] float32 workspace owned by the caller; on return it holds D.
+ *   d                : 64 or 128 (FA_ERR_UNSUPPORTED otherwise; FA_F32 and FA_FP8_E4M3 likewise).
+ * Products accumulate in float32; P and dS are rounded to `dtype` as MFMA operands.  Deterministic:
+ * no atomics (dq comes from one pass over the key tiles, dk and dv from one over the query tiles).
+ * Returns an fa_status.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, float* delta,
+           int B, int H, int N, int d, int causal, float scale, int dtype, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* fa_status_str(int status);
 

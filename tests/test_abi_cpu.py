@@ -43,7 +43,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert set(names) == {"fa_fwd", "fa_fwd_ex", "fa_fp8_prep", "fa_status_str", "fa_last_error",
+    assert set(names) == {"fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_fp8_prep", "fa_status_str", "fa_last_error",
                           "fa_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -100,3 +100,33 @@ def test_prep_validation_statuses(lib):
     assert f(big, 2, big * 2, big * 3, ctypes.cast(good, vp), 64, 0, 64, 128, None) == FA_OK
     assert f(None, 2, big * 2, big * 3, ctypes.cast(good, vp), 64, 1, 64, 128, None) == FA_ERR_NULL
     assert f(big + 4, 2, big * 2, big * 3, None, 64, 1, 64, 128, None) == FA_ERR_ALIGN
+
+
+def test_bwd_validation_statuses(lib):
+    f = lib.fa_bwd
+    vp = ctypes.c_void_p
+    f.argtypes = [vp] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int, vp]
+    f.restype = ctypes.c_int
+    big = 1 << 24  # fake, 16-aligned, disjoint 16 MiB regions: validation never dereferences them
+    ptrs = [big * (i + 1) for i in range(10)]  # q k v o lse dout dq dk dv delta
+
+    def call(p=None, B=1, H=2, N=64, d=128, causal=0, scale=0.1, dtype=2):
+        return f(*(p or ptrs), B, H, N, d, causal, scale, dtype, None)
+
+    # every call below fails validation (or is empty), so nothing is ever launched on these fake pointers
+    assert call(dtype=0) == FA_ERR_UNSUPPORTED   # float32 backward is not built
+    assert call(dtype=3) == FA_ERR_UNSUPPORTED   # nor fp8
+    assert call(dtype=9) == FA_ERR_DTYPE
+    assert call(d=256) == FA_ERR_UNSUPPORTED
+    assert call(causal=3) == FA_ERR_ARG
+    assert call(scale=float("nan")) == FA_ERR_ARG
+    assert call(N=-2) == FA_ERR_SHAPE
+    assert call(N=0, p=[None] * 10) == FA_OK      # empty problem: no-op
+    assert call(p=ptrs[:9] + [None]) == FA_ERR_NULL
+    assert call(p=ptrs[:4] + [big * 5 + 4] + ptrs[5:]) == FA_ERR_ALIGN
+    alias = list(ptrs)
+    alias[6] = ptrs[0]  # dq aliases q
+    assert call(p=alias) == FA_ERR_ARG
+    alias = list(ptrs)
+    alias[7] = ptrs[8]  # dk aliases dv
+    assert call(p=alias) == FA_ERR_ARG
