@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
-"""Benchmark of the exact tiled attention forward on one MI355X.
+"""Benchmark of the exact tiled attention forward (and, with --bwd, backward) on one MI355X.
 
 One step = one full forward pass (work partition, Q/K/V tiles, scores, mask, online softmax, P*V,
 epilogue; for the fp8 workload also the three preparation launches) over one batch of seeded
 synthetic inputs already resident in HBM.  Default workload: bf16 B16 H16 N1024 d128 non-causal.
+With --bwd a step is one backward pass (delta, dQ, dK/dV launches) from the forward's saved o and
+lse, counted as 10*B*H*N^2*d flops (/2 causal).
 
 Prints ONE JSON line (rank 0):
   metric/value/unit         attention fwd TFLOP/s = 4*B*H*N^2*d (/2 causal) / time per step
@@ -97,11 +99,11 @@ def ingest_counters(cfg_id: int, fetch_csv: str, write_csv: str) -> int:
     return 0
 
 
-def cpu_baseline(w, seed: int, budget_s: float = 12.0):
+def cpu_baseline(w, seed: int, budget_s: float = 12.0, bwd: bool = False):
     """Time the float64 oracle on whole heads of the workload until ~budget_s of CPU work."""
     import numpy as np
 
-    from oracle import attention_rows
+    from oracle import attention_bwd_rows, attention_rows
     from synth import gen_qkv
 
     try:
@@ -112,14 +114,17 @@ def cpu_baseline(w, seed: int, budget_s: float = 12.0):
         threads = os.cpu_count() or 1
     # one head's worth of inputs (the generator draws whole tensors; take the first heads)
     q, k, v = gen_qkv(1, min(w.H, 4), w.N, w.d, "bf16" if w.dtype == "fp8" else w.dtype, seed)
-    per_head = 4.0 * w.N * w.N * w.d / (2.0 if w.causal else 1.0)
+    per_head = (10.0 if bwd else 4.0) * w.N * w.N * w.d / (2.0 if w.causal else 1.0)
     done_flops, heads, t0 = 0.0, 0, time.perf_counter()
     chunk = 1024
     while True:
         h = heads % q.shape[1]
-        for r0 in range(0, w.N, chunk):
-            rows = np.arange(r0, min(w.N, r0 + chunk))
-            attention_rows(q[0, h], k[0, h], v[0, h], rows, w.causal, w.scale)
+        if bwd:
+            attention_bwd_rows(q[0, h], k[0, h], v[0, h], q[0, (h + 1) % q.shape[1]], w.causal, w.scale)
+        else:
+            for r0 in range(0, w.N, chunk):
+                rows = np.arange(r0, min(w.N, r0 + chunk))
+                attention_rows(q[0, h], k[0, h], v[0, h], rows, w.causal, w.scale)
         heads += 1
         done_flops += per_head
         if time.perf_counter() - t0 >= budget_s or heads >= 512:
@@ -130,7 +135,8 @@ def cpu_baseline(w, seed: int, budget_s: float = 12.0):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{heads} (b,h) heads of the workload (float64 NumPy/OpenBLAS, full score rows), "
+        "sample": f"{heads} (b,h) heads of the workload ({'backward, ' if bwd else ''}float64 NumPy/OpenBLAS, "
+                  f"full score rows), "
                   f"{dt:.1f} s",
     }
 
@@ -143,6 +149,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (dQ, dK, dV from the saved lse) instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -166,7 +174,19 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     seed = w.cfg_id
-    if w.dtype == "fp8":
+    if args.bwd:
+        if w.dtype not in ("bf16", "f16") or w.d not in (64, 128):
+            print(f"the backward pass covers bf16/fp16 with d 64 or 128, not workload {w.cfg_id}", file=sys.stderr)
+            return 2
+        q, k, v = (t.to(dev) for t in gen_qkv(w.B, w.H, w.N, w.d, w.dtype, seed))
+        do = gen_qkv(w.B, w.H, w.N, w.d, w.dtype, seed + 1000)[0].to(dev)
+        o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def step():
+            return fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, delta=delta)
+    elif w.dtype == "fp8":
         qs, ks, vs, signs = gen_fp8_workload(w, seed)
         qs, ks, vs = qs.to(dev), ks.to(dev), vs.to(dev)
 
@@ -203,13 +223,14 @@ def main() -> int:
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
 
-    flops = w.flops
+    flops = w.flops * (2.5 if args.bwd else 1.0)  # backward: dS, dQ, dK, dV and the recomputed S = 10 N^2 d
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = load_traffic(w.cfg_id, w.dtype)
+    traffic = None if args.bwd else load_traffic(w.cfg_id, w.dtype)
     line = {
-        "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, /2 causal) and % of MI355X MFMA peak",
+        "metric": ("attention bwd TFLOP/s (10*B*H*N^2*d, /2 causal) and % of MI355X MFMA peak" if args.bwd else
+                   "attention fwd TFLOP/s (4*B*H*N^2*d, /2 causal) and % of MI355X MFMA peak"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -221,7 +242,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "f16": "f16", "f32": "f32", "fp8": "fp8_e4m3"}[w.dtype],
         "data": "synthetic (seeded N(0,1), resident in HBM)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+        "config": {"workload": w.name.replace(" fwd", " bwd") if args.bwd else w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "parallelism": "single GPU"},
         "roofline": {
             "bound": "mfma",
@@ -240,7 +261,7 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize(dev)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, seed)
+        line["cpu_baseline"] = cpu_baseline(w, seed, bwd=args.bwd)
     print(json.dumps(line), flush=True)
     return 0
 

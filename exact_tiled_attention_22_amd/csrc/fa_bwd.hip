@@ -375,7 +375,7 @@ struct BwdKV {
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256, 2) void bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                        const T* __restrict__ V, const T* __restrict__ dO,
                                                        const float* __restrict__ LSE, const float* __restrict__ Dl,
                                                        T* __restrict__ dQ, int N, int BH, int ntq, float c,
