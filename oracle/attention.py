@@ -114,3 +114,21 @@ def attention_bwd_ref(q, k, v, do, causal: bool, scale: float):
     for idx in np.ndindex(*q.shape[:-2]):
         dq[idx], dk[idx], dv[idx] = attention_bwd_rows(q[idx], k[idx], v[idx], do[idx], causal, scale)
     return dq, dk, dv
+
+
+def attention_rect(qh, kh, vh, causal: bool, scale: float):
+    """Attention of Nq queries against Nk >= Nq keys for ONE head (the decode shape: the queries are the
+    last Nq positions of a sequence whose keys are all cached).  Causal means query i sees keys
+    j <= i + (Nk - Nq) (the mask aligned to the end of the key sequence); with Nq == Nk this is the
+    lower-triangular mask of attention_rows.  Returns (O [Nq, d], lse [Nq]) in float64, full score
+    rows, same definition as attention_rows.
+    """
+    qh, kh, vh = _f64(qh), _f64(kh), _f64(vh)
+    nq, nk = qh.shape[0], kh.shape[0]
+    s = float(scale) * (qh @ kh.T)
+    if causal:
+        s = np.where(np.arange(nk)[None, :] <= np.arange(nq)[:, None] + (nk - nq), s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    return (e @ vh) / l, m[:, 0] + np.log(l[:, 0])
