@@ -12,8 +12,10 @@ from .binding import (  # noqa: F401
     FaError,
     abi_version,
     bwd,
+    decode_workspace_bytes,
     fp8_prep,
     fwd,
+    fwd_decode,
     last_error,
     lib,
     status_str,

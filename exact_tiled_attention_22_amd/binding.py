@@ -58,6 +58,11 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_ex.restype = i
     L.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
     L.fa_bwd.restype = i
+    L.fa_fwd_decode.argtypes = [vp] * 5 + [i] * 6 + [f, i, vp, ctypes.c_size_t, vp]
+    L.fa_fwd_decode.restype = i
+    L.fa_decode_workspace_bytes.argtypes = [i] * 5
+    L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_bwd.restype = i
     L.fa_fp8_prep.argtypes = [vp, i, vp, vp, vp, i, i, i, i, vp]
     L.fa_fp8_prep.restype = i
     L.fa_status_str.argtypes = [i]
@@ -135,6 +140,34 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
     del keep
     _check(st, "fa_fwd_ex")
     return out, (lse if return_lse else None)
+
+
+def decode_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    return int(lib().fa_decode_workspace_bytes(B, H, Nq, Nk, d))
+
+
+def fwd_decode(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None, workspace=None):
+    """Decode-shape attention through fa_fwd_decode: q [B, H, Nq, d] (Nq <= 32, the last Nq positions)
+    against k, v [B, H, Nk, d].  Returns (o, lse).  ``workspace`` is a uint8 device tensor of at least
+    decode_workspace_bytes(...) bytes (allocated when not given)."""
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v must be contiguous 4-D GPU tensors")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must be [B, H, Nk, d] of q's dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = decode_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib().fa_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, int(bool(causal)),
+                             float(scale), DTYPE_CODE[q.dtype], _ptr(workspace), workspace.numel(), _stream(q.device))
+    _check(st, "fa_fwd_decode")
+    return out, lse
 
 
 def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = None, dq=None, dk=None, dv=None,

@@ -1,0 +1,246 @@
+// fa_decode.hip — attention for a few queries against a long cached key/value sequence (decode).
+//
+// The pages tie the method's memory savings to longer key/value caches at serving time (Flash Attention
+// glossary, "/02 Warum ist Flash Attention wichtig?": bigger caches and longer context on the same
+// GPU; concept card "Kernpunkte": activation memory at 4k context).  With Nq <= 32 queries per (b, h)
+// there is no query tiling to spread over the chip, so the keys are split instead:
+//   1. decode_split_kernel: every wave of every workgroup owns one contiguous chunk of the keys of one
+//      (b, h) and runs the forward pass's tile loop over it (32-key tiles through the wave's own two
+//      LDS stages, scores S^T = K Q^T, online softmax in base 2, O^T += V^T P^T), then stores its
+//      partial result: O_c (normalised, float32) and lse_c = m + log2 l (base 2) per query;
+//   2. decode_merge_kernel: per (b, h, query), lse = log2 sum_c 2^lse_c and O = sum_c 2^(lse_c - lse) O_c,
+//      which is the same softmax over the union of the chunks.
+// The waves share nothing, so there is no workgroup barrier; each waits only for its own copies.
+// Causal: query i (of Nq) sees keys j <= i + Nk - Nq (the queries are the last Nq positions).
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr float kTauD = 8.0f;  // lazy rescale threshold (log2 units), as in the forward pass
+
+template <int CPR>
+__device__ __forceinline__ int dswz(int row) {
+    if constexpr (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+template <typename T, int D, bool CAUSAL>
+struct Decode {
+    using VT = Vec<T>;
+    using x8 = typename VT::x8;
+    using x4 = typename VT::x4;
+    static constexpr int NW = 4, BN = 32, CPR = D / 8, KS = D / 16, CB = D / 32;
+    static constexpr int TILE = BN * CPR * 16;           // one K or V tile
+    static constexpr int WAVE_LDS = 4 * TILE;             // K0 | V0 | K1 | V1 per wave
+    static constexpr int LDS_BYTES = NW * WAVE_LDS;
+    static constexpr int LPT = BN * CPR / 64;             // copies per lane per tile
+
+    // copy rows [r0, r0 + BN) of a [Nk, D] slice into this wave's tile (rows >= Nk repeat row Nk - 1)
+    static __device__ __forceinline__ void copy(const T* __restrict__ src, int r0, int Nk, uint32_t lds, int lane) {
+#pragma unroll
+        for (int t = 0; t < LPT; ++t) {
+            const int slot = t * 64 + lane;
+            const int row = slot / CPR;
+            const int c = (slot % CPR) ^ dswz<CPR>(row);
+            dma16(src + (size_t)min(r0 + row, Nk - 1) * D + c * 8, lds + (uint32_t)(t * 64 * 16));
+        }
+    }
+
+    static __device__ __forceinline__ void run(const T* __restrict__ Q, const T* __restrict__ K,
+                                               const T* __restrict__ V, float* __restrict__ Op,
+                                               float* __restrict__ Lp, int Nq, int Nk, int nsplit, int chunk,
+                                               float c, uint32_t qflip, char* smem) {
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int n32 = lane & 31, h = lane >> 5;
+        const int bh = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
+        const int nc = nsplit * NW, ci = split * NW + wave;      // chunk index of this wave
+        const int j0 = ci * chunk, j1 = min(Nk, j0 + chunk);     // its keys
+        const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(smem)) + wave * WAVE_LDS;
+        const char* wl = smem + wave * WAVE_LDS;
+        const T* Kh = K + (size_t)bh * Nk * D;
+        const T* Vh = V + (size_t)bh * Nk * D;
+        const int query = n32, qrow = min(query, Nq - 1);
+        const int last_key = CAUSAL ? query + Nk - Nq : Nk - 1;  // last key visible to this lane's query
+
+        const int kperm = ((n32 >> 4) & 1) * 16 + ((n32 >> 2) & 1) * 8 + ((n32 >> 3) & 1) * 4 + (n32 & 3);
+        const int i16 = lane & 15, G = lane >> 4;
+        const int vrow = (G >> 1) * 8 + (i16 >> 2), vcc = (G & 1) * 2 + ((i16 & 3) >> 1), vb = (i16 & 1) * 8;
+
+        x8 qreg[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            i32x4 raw = *(const i32x4*)(Q + ((size_t)bh * Nq + qrow) * D + ks * 16 + h * 8);
+            raw ^= (int)qflip;
+            qreg[ks] = __builtin_bit_cast(x8, raw);
+        }
+        const int ntile = j1 > j0 ? (j1 - j0 + BN - 1) / BN : 0;
+        if (ntile > 0) {
+            copy(Kh, j0, Nk, lbase, lane);
+            copy(Vh, j0, Nk, lbase + TILE, lane);
+        }
+        f32x16 oacc[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16{};
+        float m_run = -INFINITY, l_run = 0.0f;
+
+        for (int t = 0; t < ntile; ++t) {
+            const int st = t & 1;
+            const int kv0 = j0 + t * BN;
+            if (t + 1 < ntile) {
+                // the stage about to be refilled was last read by this wave's previous tile
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                copy(Kh, kv0 + BN, Nk, lbase + (st ^ 1) * 2 * TILE, lane);
+                copy(Vh, kv0 + BN, Nk, lbase + (st ^ 1) * 2 * TILE + TILE, lane);
+                wait_vmcnt<2 * LPT>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            const char* kl = wl + st * 2 * TILE;
+            const char* vl = kl + TILE;
+            // S^T = K Q^T for 32 keys: register r holds key kv0 + (r/8)*16 + h*8 + r%8
+            f32x16 s = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const x8 kop = *(const x8*)(kl + (kperm * CPR + ((2 * ks + h) ^ dswz<CPR>(kperm))) * 16);
+                s = VT::mfma(kop, qreg[ks], s);
+            }
+            if (kv0 + BN > j1 || kv0 + BN - 1 > last_key) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kv0 + (r >> 3) * 16 + h * 8 + (r & 7);
+                    if (key >= j1 || key > last_key) s[r] = -INFINITY;
+                }
+            }
+            float mx = s[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+            const float mt = halves_max(mx) * c;
+            if (__ballot(mt > m_run + kTauD)) {
+                const float mn = fmaxf(m_run, mt);
+                const float alpha = fast_exp2(m_run - mn);
+                m_run = mn;
+                l_run *= alpha;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
+            }
+            // while no key of the chunk has been visible to this query, m_run is -inf and every score
+            // is -inf: use 0 as the offset so the weights come out 0 (not exp2 of -inf + inf)
+            const float negm = m_run == -INFINITY ? 0.0f : -m_run;
+            float e[16];
+            float sum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                e[r] = fast_exp2(__builtin_fmaf(s[r], c, negm));
+                sum += e[r];
+            }
+            l_run += sum;
+            const x8 p0 = VT::pack(e), p1 = VT::pack(e + 8);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+                for (int sp = 0; sp < 2; ++sp) {
+                    const int r0 = sp * 16;
+                    const int row0 = r0 + vrow, row1 = r0 + 4 + vrow;
+                    const x4 lo = VT::read_tr(vl + (row0 * CPR + ((cb * 4 + vcc) ^ dswz<CPR>(row0))) * 16 + vb);
+                    const x4 hi = VT::read_tr(vl + (row1 * CPR + ((cb * 4 + vcc) ^ dswz<CPR>(row1))) * 16 + vb);
+                    oacc[cb] = VT::mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), sp ? p1 : p0,
+                                        oacc[cb]);
+                }
+            }
+        }
+        // partial result of this chunk: O_c = O / l, lse_c = m + log2 l (base 2); an empty chunk
+        // (no visible key) stores lse_c = -inf and O_c = 0
+        const float lt = halves_sum(l_run);
+        if (query < Nq) {
+            const size_t slot = ((size_t)bh * nc + ci) * Nq + query;
+            const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+            float* orow = Op + slot * D;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = oacc[cb][g * 4 + e] * inv;
+                    *(f32x4*)(orow + cb * 32 + g * 8 + h * 4) = out;
+                }
+            if (h == 0) Lp[slot] = lt > 0.0f ? m_run + __log2f(lt) : -INFINITY;
+        }
+    }
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void decode_split_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                              const T* __restrict__ V, float* __restrict__ Op,
+                                                              float* __restrict__ Lp, int Nq, int Nk, int nsplit,
+                                                              int chunk, float c, uint32_t qflip) {
+    __shared__ __attribute__((aligned(1024))) char smem[Decode<T, D, CAUSAL>::LDS_BYTES];
+    Decode<T, D, CAUSAL>::run(Q, K, V, Op, Lp, Nq, Nk, nsplit, chunk, c, qflip, smem);
+}
+
+// one workgroup of D threads per (b, h, query): thread t owns output column t
+template <typename T, int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ Op, const float* __restrict__ Lp,
+                                                         T* __restrict__ O, float* __restrict__ LSE, int Nq, int nc) {
+    const int bh = blockIdx.x / Nq, query = blockIdx.x % Nq, col = threadIdx.x;
+    const size_t base = (size_t)bh * nc * Nq + query;
+    float M = -INFINITY;
+    for (int i = 0; i < nc; ++i) M = fmaxf(M, Lp[base + (size_t)i * Nq]);
+    float L = 0.0f, acc = 0.0f;
+    for (int i = 0; i < nc; ++i) {
+        const float lc = Lp[base + (size_t)i * Nq];
+        const float w = lc == -INFINITY ? 0.0f : fast_exp2(lc - M);
+        L += w;
+        acc = __builtin_fmaf(w, Op[(base + (size_t)i * Nq) * D + col], acc);
+    }
+    O[((size_t)bh * Nq + query) * D + col] = (T)(acc / L);
+    if (LSE != nullptr && col == 0) LSE[(size_t)bh * Nq + query] = (M + __log2f(L)) * 0.69314718055994531f;
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_decode_t(const void* q, const void* k, const void* v, void* o, float* lse, float* work, int BH,
+                           int Nq, int Nk, int nsplit, int chunk, float c, uint32_t qflip, hipStream_t stream) {
+    const int nc = nsplit * Decode<T, D, CAUSAL>::NW;
+    float* Op = work;
+    float* Lp = work + (size_t)BH * nc * Nq * D;
+    const long long nwg = (long long)BH * nsplit, nm = (long long)BH * Nq;
+    if (nwg > 0x7fffffffLL || nm > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_split_kernel<T, D, CAUSAL>), dim3((unsigned)nwg), dim3(256), 0, stream, (const T*)q,
+                       (const T*)k, (const T*)v, Op, Lp, Nq, Nk, nsplit, chunk, c, qflip);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)nm), dim3(D), 0, stream, (const float*)Op,
+                       (const float*)Lp, (T*)o, lse, Nq, nc);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_decode_dt(const void* q, const void* k, const void* v, void* o, float* lse, float* work, int BH,
+                            int Nq, int Nk, int d, bool causal, int nsplit, int chunk, float c, uint32_t qflip,
+                            hipStream_t stream) {
+    switch (d) {
+        case 64:
+            return causal ? launch_decode_t<T, 64, true>(q, k, v, o, lse, work, BH, Nq, Nk, nsplit, chunk, c, qflip, stream)
+                          : launch_decode_t<T, 64, false>(q, k, v, o, lse, work, BH, Nq, Nk, nsplit, chunk, c, qflip, stream);
+        case 128:
+            return causal ? launch_decode_t<T, 128, true>(q, k, v, o, lse, work, BH, Nq, Nk, nsplit, chunk, c, qflip, stream)
+                          : launch_decode_t<T, 128, false>(q, k, v, o, lse, work, BH, Nq, Nk, nsplit, chunk, c, qflip, stream);
+        default:
+            return hipErrorNotSupported;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_16(bool is_bf16, const void* q, const void* k, const void* v, void* o, float* lse, float* work,
+                            int BH, int Nq, int Nk, int d, bool causal, int nsplit, int chunk, float c, uint32_t qflip,
+                            hipStream_t stream) {
+    return is_bf16 ? launch_decode_dt<__bf16>(q, k, v, o, lse, work, BH, Nq, Nk, d, causal, nsplit, chunk, c, qflip, stream)
+                   : launch_decode_dt<_Float16>(q, k, v, o, lse, work, BH, Nq, Nk, d, causal, nsplit, chunk, c, qflip,
+                                                stream);
+}
+
+}  // namespace fa

@@ -53,6 +53,26 @@ int check_sizes(long long BH, long long N, long long d) {
     return FA_OK;
 }
 
+// Key split of the decode path: enough workgroups (4 waves each) to cover the 256 CUs, chunks of at
+// least 64 keys per wave, chunk length a multiple of the 32-key tile.
+void decode_split(long long BH, long long Nk, int* nsplit, int* chunk) {
+    long long ns = (256 + BH - 1) / BH;
+    const long long maxs = Nk / (4 * 64);
+    if (ns > maxs) ns = maxs;
+    if (ns < 1) ns = 1;
+    const long long nc = ns * 4;
+    long long ck = (Nk + nc - 1) / nc;
+    ck = (ck + 31) / 32 * 32;
+    *nsplit = static_cast<int>(ns);
+    *chunk = static_cast<int>(ck);
+}
+
+size_t decode_bytes(long long BH, int Nq, int Nk, int d) {
+    int ns = 1, ck = 32;
+    decode_split(BH, Nk, &ns, &ck);
+    return static_cast<size_t>(BH) * ns * 4 * Nq * (d + 1) * sizeof(float);
+}
+
 int from_hip(hipError_t e, const char* what) {
     if (e == hipSuccess) return FA_OK;
     if (e == hipErrorNotSupported) return fail(FA_ERR_UNSUPPORTED, "%s: no kernel instance for this request", what);
@@ -146,6 +166,49 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d, int causal,
            float scale, int dtype, void* stream) {
     return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, nullptr, stream);
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
+    return decode_bytes(static_cast<long long>(B) * H, Nq, Nk, d);
+}
+
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                  int d, int causal, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    if (dtype != FA_F16 && dtype != FA_BF16) {
+        if (elem_bytes(dtype) == 0) return fail(FA_ERR_DTYPE, "dtype code %d is not a fa_dtype", dtype);
+        return fail(FA_ERR_UNSUPPORTED, "fa_fwd_decode dtype %d (supported: FA_F16, FA_BF16)", dtype);
+    }
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return fail(FA_ERR_SHAPE, "negative size B=%d H=%d Nq=%d Nk=%d", B, H, Nq, Nk);
+    if (causal != 0 && causal != 1) return fail(FA_ERR_ARG, "causal must be 0 or 1, got %d", causal);
+    if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale must be finite");
+    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "fa_fwd_decode head dimension d=%d (supported: 64, 128)", d);
+    if (Nq > 32) return fail(FA_ERR_UNSUPPORTED, "fa_fwd_decode takes at most 32 queries per head, got %d", Nq);
+    if (Nq > Nk) return fail(FA_ERR_SHAPE, "fewer keys (%d) than queries (%d)", Nk, Nq);
+    const long long BH = static_cast<long long>(B) * H;
+    if (BH == 0 || Nq == 0) return FA_OK;
+    if (int st = check_sizes(BH, Nk, d)) return st;
+    if (!q || !k || !v || !o || !workspace) return fail(FA_ERR_NULL, "q, k, v, o and workspace must be non-NULL");
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) || misaligned(workspace))
+        return fail(FA_ERR_ALIGN, "q, k, v, o, lse and workspace must be 16-byte aligned");
+    const size_t need = decode_bytes(BH, Nq, Nk, d);
+    if (workspace_bytes < need) return fail(FA_ERR_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    const size_t qb = static_cast<size_t>(BH) * Nq * d * 2, kb = static_cast<size_t>(BH) * Nk * d * 2;
+    if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb))
+        return fail(FA_ERR_ARG, "o must not overlap q, k or v");
+    if (overlaps(workspace, need, q, qb) || overlaps(workspace, need, k, kb) || overlaps(workspace, need, v, kb) ||
+        overlaps(workspace, need, o, qb) || (lse && overlaps(workspace, need, lse, static_cast<size_t>(BH) * Nq * 4)))
+        return fail(FA_ERR_ARG, "workspace must not overlap any tensor");
+    if (lse && overlaps(lse, static_cast<size_t>(BH) * Nq * 4, o, qb)) return fail(FA_ERR_ARG, "lse must not overlap o");
+    float c = static_cast<float>(std::fabs(static_cast<double>(scale)) * 1.4426950408889634);
+    if (!(c >= 1e-30f)) c = 1e-30f;
+    int ns = 1, ck = 32;
+    decode_split(BH, Nk, &ns, &ck);
+    return from_hip(fa::launch_decode_16(dtype == FA_BF16, q, k, v, o, lse, static_cast<float*>(workspace),
+                                         static_cast<int>(BH), Nq, Nk, d, causal != 0, ns, ck, c,
+                                         std::signbit(scale) ? 0x80008000u : 0u, reinterpret_cast<hipStream_t>(stream)),
+                    dtype == FA_BF16 ? "fa_fwd_decode(bf16)" : "fa_fwd_decode(f16)");
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,

@@ -34,4 +34,10 @@ hipError_t launch_bwd_16(bool is_bf16, const void* q, const void* k, const void*
                          const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int N, int d,
                          bool causal, float scale, hipStream_t stream);
 
+// decode (bf16 / fp16, d in {64, 128}, Nq <= 32): split the keys over nsplit workgroups of 4 waves per
+// (b, h), chunks of `chunk` keys per wave; work = float32 [BH, 4 nsplit, Nq, d] then [BH, 4 nsplit, Nq].
+hipError_t launch_decode_16(bool is_bf16, const void* q, const void* k, const void* v, void* o, float* lse, float* work,
+                            int BH, int Nq, int Nk, int d, bool causal, int nsplit, int chunk, float c, uint32_t qflip,
+                            hipStream_t stream);
+
 }  // namespace fa

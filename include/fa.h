@@ -29,6 +29,7 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -112,6 +113,26 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
  */
 int fa_fp8_prep(const void* x, int x_dtype, void* x8, float* scales,
                 const int8_t* hadamard, int block, int BH, int N, int d, void* stream);
+
+/*
+ * Attention of a few queries against a long cached key/value sequence (decode).  The pages tie the
+ * method's memory savings to bigger key/value caches and longer context at serving time (Flash
+ * Attention glossary, "/02 Warum ist Flash Attention wichtig?").  Same definition as fa_fwd with
+ * Nq queries and Nk >= Nq keys per (b, h):
+ *   q, o : DEVICE [B,H,Nq,d];  k, v : DEVICE [B,H,Nk,d];  lse : DEVICE [B,H,Nq] float32 or NULL.
+ *   causal : 1 = query i sees keys j <= i + Nk - Nq (the queries are the last Nq positions).
+ *   dtype : FA_F16 or FA_BF16; d : 64 or 128; 1 <= Nq <= 32 (FA_ERR_UNSUPPORTED otherwise).
+ *   workspace : DEVICE scratch of at least fa_decode_workspace_bytes(B, H, Nq, Nk, d) bytes, owned by
+ *               the caller, 16-byte aligned, overlapping no tensor; its contents on return are
+ *               unspecified.  Calls that share a workspace must not overlap in time.
+ * The keys are split into chunks handled by independent waves (per-chunk online softmax), and a
+ * second launch merges the chunks' (O, lse) pairs; float32 accumulation, P rounded to `dtype`.
+ * Returns an fa_status.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Nq, int Nk, int d, int causal, float scale, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Attention backward: the gradients of fa_fwd's output with respect to q, k and v for a given output

@@ -43,8 +43,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert set(names) == {"fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_fp8_prep", "fa_status_str", "fa_last_error",
-                          "fa_abi_version"}
+    assert set(names) == {"fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_fwd_decode", "fa_decode_workspace_bytes",
+                          "fa_fp8_prep", "fa_status_str", "fa_last_error", "fa_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -130,3 +130,37 @@ def test_bwd_validation_statuses(lib):
     alias = list(ptrs)
     alias[7] = ptrs[8]  # dk aliases dv
     assert call(p=alias) == FA_ERR_ARG
+
+
+def test_decode_validation_statuses(lib):
+    f = lib.fa_fwd_decode
+    vp = ctypes.c_void_p
+    f.argtypes = [vp] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp]
+    f.restype = ctypes.c_int
+    ws = lib.fa_decode_workspace_bytes
+    ws.argtypes = [ctypes.c_int] * 5
+    ws.restype = ctypes.c_size_t
+    need = ws(2, 4, 1, 1000, 128)
+    assert need > 0 and need % 16 == 0
+    assert ws(0, 4, 1, 1000, 128) == 0
+    big = 1 << 26
+    p = [big * (i + 1) for i in range(5)]  # q k v o lse
+    w = big * 7
+
+    def call(pp=None, B=2, H=4, Nq=1, Nk=1000, d=128, causal=0, scale=0.1, dtype=2, work=w, nbytes=None):
+        return f(*(pp or p), B, H, Nq, Nk, d, causal, scale, dtype, work, need if nbytes is None else nbytes, None)
+
+    # every call below fails validation (or is empty): nothing is launched on these fake pointers
+    assert call(dtype=0) == FA_ERR_UNSUPPORTED
+    assert call(dtype=7) == FA_ERR_DTYPE
+    assert call(d=256) == FA_ERR_UNSUPPORTED
+    assert call(Nq=33, Nk=1000) == FA_ERR_UNSUPPORTED
+    assert call(Nq=5, Nk=4) == FA_ERR_SHAPE
+    assert call(causal=2) == FA_ERR_ARG
+    assert call(scale=float("inf")) == FA_ERR_ARG
+    assert call(nbytes=need - 1) == FA_ERR_ARG
+    assert call(work=None) == FA_ERR_NULL
+    assert call(work=w + 8) == FA_ERR_ALIGN
+    assert call(work=p[1]) == FA_ERR_ARG  # workspace overlaps k
+    assert call(pp=[p[0], p[1], p[2], p[0], p[4]]) == FA_ERR_ARG  # o aliases q
+    assert call(Nq=0) == FA_OK
