@@ -141,6 +141,61 @@ def cpu_baseline(w, seed: int, budget_s: float = 12.0, bwd: bool = False):
     }
 
 
+DECODE = {"B": 8, "H": 32, "Nq": 1, "Nk": 32768, "d": 128, "dtype": "bf16", "causal": False}
+
+
+def bench_decode(args) -> int:
+    """Decode leg: one query per (b, h) against a 32768-key bf16 cache.  HBM-bound: the metric is the
+    K/V cache bytes read per second (2 * B * H * Nk * d * 2 bytes per step)."""
+    import torch
+
+    import exact_tiled_attention_22_amd as fa
+    from synth import gen_qkv
+
+    c = DECODE
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    qf, k, v = (t.to(dev) for t in gen_qkv(c["B"], c["H"], c["Nk"], c["d"], c["dtype"], 7))
+    q = qf[:, :, c["Nk"] - c["Nq"]:, :].contiguous()
+    del qf
+    scale = 1.0 / math.sqrt(c["d"])
+    o = torch.empty_like(q)
+    lse = torch.empty((c["B"], c["H"], c["Nq"]), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_workspace_bytes(c["B"], c["H"], c["Nq"], c["Nk"], c["d"]), dtype=torch.uint8, device=dev)
+
+    def step():
+        return fa.fwd_decode(q, k, v, causal=c["causal"], scale=scale, out=o, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize(dev)
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    avg_ms = sum(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)) / args.steps
+    nbytes = 2.0 * c["B"] * c["H"] * c["Nk"] * c["d"] * 2
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    line = {
+        "metric": "decode attention K/V cache read GB/s (2*B*H*Nk*d*2 bytes per step)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1), resident in HBM)",
+        "config": {"workload": "bf16 decode B8 H32 Nq1 Nk32768 d128 non-causal", **c, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(achieved / 8000.0, 4), "traffic": None, "kernel_avg_ms": round(avg_ms, 5)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +204,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the decode path (1 query against a 32768-key cache, B8 H32 d128 bf16)")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (dQ, dK, dV from the saved lse) instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -170,6 +227,8 @@ def main() -> int:
     import exact_tiled_attention_22_amd as fa
     from synth import CONFIGS, gen_fp8_workload, gen_qkv
 
+    if args.decode:
+        return bench_decode(args)
     w = CONFIGS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
