@@ -5,7 +5,8 @@ One step = one full forward pass (work partition, Q/K/V tiles, scores, mask, onl
 epilogue; for the fp8 workload also the three preparation launches) over one batch of seeded
 synthetic inputs already resident in HBM.  Default workload: bf16 B16 H16 N1024 d128 non-causal.
 With --bwd a step is one backward pass (delta, dQ, dK/dV launches) from the forward's saved o and
-lse, counted as 10*B*H*N^2*d flops (/2 causal).
+lse, counted as 10*B*H*N^2*d flops (/2 causal).  --decode times the decode path (K/V cache read
+GB/s); --naive times the unfused path (scores, softmax, P*V through HBM) beside the fused kernel.
 
 Prints ONE JSON line (rank 0):
   metric/value/unit         attention fwd TFLOP/s = 4*B*H*N^2*d (/2 causal) / time per step
@@ -196,6 +197,93 @@ def bench_decode(args) -> int:
     return 0
 
 
+def bench_naive(args, w) -> int:
+    """Unfused comparison leg: S = scale Q K^T (float32) -> softmax -> P V, each step three launches with
+    the N x N matrices in HBM, each launch timed with HIP events; the fused kernel is timed beside it on
+    the same inputs.  Every stage is HBM-bound: the roofline is the slowest stage's algorithmic bytes
+    per second against 8 TB/s."""
+    import torch
+
+    import exact_tiled_attention_22_amd as fa
+    from synth import gen_qkv
+
+    if w.dtype not in ("bf16", "f16"):
+        print(f"the unfused path covers bf16/fp16, not workload {w.cfg_id}", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (t.to(dev) for t in gen_qkv(w.B, w.H, w.N, w.d, w.dtype, w.cfg_id))
+    ld = fa.naive_row_stride(w.N)
+    s = torch.empty((w.B, w.H, w.N, ld), dtype=torch.float32, device=dev)
+    p = torch.empty((w.B, w.H, w.N, ld), dtype=q.dtype, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    n = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        fa.naive_scores(q, k, scale=w.scale, s=s)
+        if e: e[1].record(stream)
+        fa.naive_softmax(s, dtype=q.dtype, causal=w.causal, p=p, lse=lse)
+        if e: e[2].record(stream)
+        fa.naive_pv(p, v, out=o)
+        if e: e[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(ev[i])
+    torch.cuda.synchronize(dev)
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / n
+    stage_ms = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n)) / n for j in range(3)]
+
+    # the fused kernel on the same inputs, same protocol
+    o2 = torch.empty_like(q)
+    lse2 = torch.empty_like(lse)
+    for _ in range(args.warmup):
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o2, lse=lse2)
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    for _ in range(n):
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o2, lse=lse2)
+    torch.cuda.synchronize(dev)
+    fused_ms = (time.perf_counter() - t1) * 1e3 / n
+
+    e = 2
+    BH, N, d = w.B * w.H, w.N, w.d
+    visible = N * (N + 1) / 2 if w.causal else float(N) * N
+    stage_bytes = [BH * (2 * N * d * e + 4.0 * N * N),            # read Q, K; write S
+                   BH * (4.0 * visible + e * N * ld),              # read the visible S; write P (with padding)
+                   BH * (e * N * ld + 2 * e * N * d)]              # read P, V; write O
+    names = ["naive_scores_kernel", "naive_softmax_kernel", "naive_pv_kernel"]
+    stages = {nm: {"avg_ms": round(t, 5), "GB/s": round(b / (t * 1e-3) / 1e9, 1), "bytes": b}
+              for nm, t, b in zip(names, stage_ms, stage_bytes)}
+    dom = max(range(3), key=lambda j: stage_ms[j])
+    achieved = stage_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    line = {
+        "metric": "unfused attention fwd TFLOP/s (4*B*H*N^2*d, /2 causal; S and P through HBM)",
+        "value": round(w.flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": n, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1), resident in HBM)",
+        "config": {"workload": w.name.replace(" fwd", " unfused fwd"), "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(achieved, 1), "peak": 8000.0,
+                     "unit": "GB/s", "frac": round(achieved / 8000.0, 4), "traffic": None,
+                     "kernel_avg_ms": round(stage_ms[dom], 5)},
+        "stages": stages,
+        "fused": {"ms_per_step": round(fused_ms, 5), "value": round(w.flops / (fused_ms * 1e-3) / 1e12, 2),
+                  "speedup_over_unfused": round(ms_per_step / fused_ms, 2)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, w.cfg_id)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +294,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", action="store_true",
                     help="time the decode path (1 query against a 32768-key cache, B8 H32 d128 bf16)")
+    ap.add_argument("--naive", action="store_true",
+                    help="time the unfused path (S and P through HBM) and the fused kernel beside it")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (dQ, dK, dV from the saved lse) instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -230,6 +320,8 @@ def main() -> int:
     if args.decode:
         return bench_decode(args)
     w = CONFIGS[args.config]
+    if args.naive:
+        return bench_naive(args, w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     seed = w.cfg_id

@@ -1,4 +1,5 @@
-"""Exact tiled attention (forward and backward) for AMD Instinct MI355X (gfx950).
+"""Exact tiled attention (forward, backward, decode, and the unfused comparison path) for AMD Instinct
+MI355X (gfx950).
 
 The compute lives in ``libfa.so`` (hand-written HIP kernels behind the C ABI of ``include/fa.h``);
 this package only loads it and marshals arguments.
@@ -16,7 +17,13 @@ from .binding import (  # noqa: F401
     fp8_prep,
     fwd,
     fwd_decode,
+    fwd_naive,
     last_error,
     lib,
+    naive_pv,
+    naive_row_stride,
+    naive_scores,
+    naive_softmax,
+    naive_workspace_bytes,
     status_str,
 )

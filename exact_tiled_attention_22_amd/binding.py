@@ -62,7 +62,18 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_decode.restype = i
     L.fa_decode_workspace_bytes.argtypes = [i] * 5
     L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
-    L.fa_bwd.restype = i
+    L.fa_naive_row_stride.argtypes = [i]
+    L.fa_naive_row_stride.restype = i
+    L.fa_naive_workspace_bytes.argtypes = [i, i, i]
+    L.fa_naive_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_naive_scores.argtypes = [vp, vp, vp, i, i, i, i, f, i, vp]
+    L.fa_naive_scores.restype = i
+    L.fa_naive_softmax.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+    L.fa_naive_softmax.restype = i
+    L.fa_naive_pv.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+    L.fa_naive_pv.restype = i
+    L.fa_fwd_naive.argtypes = [vp] * 5 + [i] * 5 + [f, i, vp, ctypes.c_size_t, vp]
+    L.fa_fwd_naive.restype = i
     L.fa_fp8_prep.argtypes = [vp, i, vp, vp, vp, i, i, i, i, vp]
     L.fa_fp8_prep.restype = i
     L.fa_status_str.argtypes = [i]
@@ -167,6 +178,78 @@ def fwd_decode(q, k, v, *, causal: bool = False, scale: float | None = None, out
     st = lib().fa_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, int(bool(causal)),
                              float(scale), DTYPE_CODE[q.dtype], _ptr(workspace), workspace.numel(), _stream(q.device))
     _check(st, "fa_fwd_decode")
+    return out, lse
+
+
+def naive_row_stride(N: int) -> int:
+    """Row stride (elements) of the unfused path's score and probability matrices: N rounded up to 64."""
+    return int(lib().fa_naive_row_stride(N))
+
+
+def naive_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(lib().fa_naive_workspace_bytes(B, H, N))
+
+
+def naive_scores(q, k, *, scale: float | None = None, s=None):
+    """Unfused step 1 through fa_naive_scores: s = scale q k^T as float32 [B, H, N, ld]."""
+    _check_qkv(q, k, k)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if s is None:
+        s = torch.empty((B, H, N, naive_row_stride(N)), dtype=torch.float32, device=q.device)
+    st = lib().fa_naive_scores(_ptr(q), _ptr(k), _ptr(s), B, H, N, d, float(scale), DTYPE_CODE[q.dtype],
+                               _stream(q.device))
+    _check(st, "fa_naive_scores")
+    return s
+
+
+def naive_softmax(s, *, dtype, causal: bool = False, p=None, lse=None):
+    """Unfused step 2 through fa_naive_softmax: p = softmax(s [+ causal mask]) of ``dtype``
+    [B, H, N, ld] (zero beyond column N) and lse [B, H, N]."""
+    if not s.is_cuda or s.dtype != torch.float32 or s.dim() != 4 or not s.is_contiguous():
+        raise ValueError("s must be a contiguous float32 [B, H, N, ld] GPU tensor")
+    B, H, N, ld = s.shape
+    if ld != naive_row_stride(N):
+        raise ValueError(f"s rows must be {naive_row_stride(N)} elements apart, got {ld}")
+    if p is None:
+        p = torch.empty(s.shape, dtype=dtype, device=s.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=s.device)
+    st = lib().fa_naive_softmax(_ptr(s), _ptr(p), _ptr(lse), B, H, N, int(bool(causal)), DTYPE_CODE[dtype],
+                                _stream(s.device))
+    _check(st, "fa_naive_softmax")
+    return p, lse
+
+
+def naive_pv(p, v, *, out=None):
+    """Unfused step 3 through fa_naive_pv: o = p v, [B, H, N, d] of v's dtype."""
+    if not (p.is_cuda and v.is_cuda and p.is_contiguous() and v.is_contiguous()) or v.dim() != 4:
+        raise ValueError("p and v must be contiguous 4-D GPU tensors")
+    B, H, N, d = v.shape
+    if p.shape != (B, H, N, naive_row_stride(N)) or p.dtype != v.dtype:
+        raise ValueError("p must be [B, H, N, ld] of v's dtype")
+    if out is None:
+        out = torch.empty_like(v)
+    st = lib().fa_naive_pv(_ptr(p), _ptr(v), _ptr(out), B, H, N, d, DTYPE_CODE[v.dtype], _stream(v.device))
+    _check(st, "fa_naive_pv")
+    return out
+
+
+def fwd_naive(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None, workspace=None):
+    """Unfused attention through fa_fwd_naive (the three steps, s and p in ``workspace``, a uint8 device
+    tensor of at least naive_workspace_bytes(B, H, N) bytes, allocated when not given).  Returns (o, lse)."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if workspace is None:
+        workspace = torch.empty(max(naive_workspace_bytes(B, H, N), 16), dtype=torch.uint8, device=q.device)
+    st = lib().fa_fwd_naive(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, int(bool(causal)),
+                            float(scale), DTYPE_CODE[q.dtype], _ptr(workspace), workspace.numel(), _stream(q.device))
+    _check(st, "fa_fwd_naive")
     return out, lse
 
 

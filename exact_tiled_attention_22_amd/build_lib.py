@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_host.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_fp8_prep.hip", "fa_bwd.hip", "fa_decode.hip"]
+SOURCES = ["fa_host.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_fp8_prep.hip", "fa_bwd.hip", "fa_decode.hip", "fa_naive.hip"]
 ARCH = "gfx950"
 
 

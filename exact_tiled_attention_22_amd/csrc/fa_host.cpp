@@ -73,6 +73,27 @@ size_t decode_bytes(long long BH, int Nq, int Nk, int d) {
     return static_cast<size_t>(BH) * ns * 4 * Nq * (d + 1) * sizeof(float);
 }
 
+// Row stride (elements) of the unfused path's score and probability matrices.
+long long naive_ld(long long N) { return (N + 63) / 64 * 64; }
+
+// Shared checks of the unfused entry points: 16-bit dtype, sizes, and that every launch index fits.
+int naive_check(int dtype, int B, int H, int N) {
+    if (dtype != FA_F16 && dtype != FA_BF16) {
+        if (elem_bytes(dtype) == 0) return fail(FA_ERR_DTYPE, "dtype code %d is not a fa_dtype", dtype);
+        return fail(FA_ERR_UNSUPPORTED, "unfused path dtype %d (supported: FA_F16, FA_BF16)", dtype);
+    }
+    if (B < 0 || H < 0 || N < 0) return fail(FA_ERR_SHAPE, "negative size B=%d H=%d N=%d", B, H, N);
+    const long long BH = static_cast<long long>(B) * H;
+    if (BH == 0 || N == 0) return FA_OK;
+    if (int st = check_sizes(BH, N, 256)) return st;
+    const double elems = static_cast<double>(BH) * static_cast<double>(N) * static_cast<double>(naive_ld(N));
+    if (elems * 6.0 > 4.0e18) return fail(FA_ERR_SHAPE, "B*H*N*ld = %.3g: the N x N matrices exceed 2^62 bytes", elems);
+    const long long nt = (N + 127) / 128;
+    if (BH * nt * nt > 0x7fffffffLL || (BH * N + 3) / 4 > 0x7fffffffLL)
+        return fail(FA_ERR_SHAPE, "B*H*N = %lld too large for the unfused path's grids", BH * N);
+    return FA_OK;
+}
+
 int from_hip(hipError_t e, const char* what) {
     if (e == hipSuccess) return FA_OK;
     if (e == hipErrorNotSupported) return fail(FA_ERR_UNSUPPORTED, "%s: no kernel instance for this request", what);
@@ -248,6 +269,92 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
     return from_hip(fa::launch_bwd_16(dtype == FA_BF16, q, k, v, o, lse, dout, dq, dk, dv, delta, static_cast<int>(BH),
                                       N, d, causal != 0, scale, reinterpret_cast<hipStream_t>(stream)),
                     dtype == FA_BF16 ? "fa_bwd(bf16)" : "fa_bwd(f16)");
+}
+
+int fa_naive_row_stride(int N) { return N <= 0 ? 0 : static_cast<int>(naive_ld(N)); }
+
+size_t fa_naive_workspace_bytes(int B, int H, int N) {
+    if (B <= 0 || H <= 0 || N <= 0) return 0;
+    return static_cast<size_t>(B) * H * N * naive_ld(N) * 6;
+}
+
+int fa_naive_scores(const void* q, const void* k, float* s, int B, int H, int N, int d, float scale, int dtype,
+                    void* stream) {
+    g_err[0] = '\0';
+    if (int st = naive_check(dtype, B, H, N)) return st;
+    if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale must be finite");
+    if (d != 64 && d != 128 && d != 256) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128, 256)", d);
+    const long long BH = static_cast<long long>(B) * H;
+    if (BH == 0 || N == 0) return FA_OK;
+    if (!q || !k || !s) return fail(FA_ERR_NULL, "q, k and s must be non-NULL");
+    if (misaligned(q) || misaligned(k) || misaligned(s)) return fail(FA_ERR_ALIGN, "q, k and s must be 16-byte aligned");
+    const size_t in = static_cast<size_t>(BH) * N * d * 2, sb = static_cast<size_t>(BH) * N * naive_ld(N) * 4;
+    if (overlaps(s, sb, q, in) || overlaps(s, sb, k, in)) return fail(FA_ERR_ARG, "s must not overlap q or k");
+    return from_hip(fa::launch_naive_scores_16(dtype == FA_BF16, q, k, s, static_cast<int>(BH), N, d,
+                                               static_cast<int>(naive_ld(N)), scale, reinterpret_cast<hipStream_t>(stream)),
+                    "fa_naive_scores");
+}
+
+int fa_naive_softmax(const float* s, void* p, float* lse, int B, int H, int N, int causal, int dtype, void* stream) {
+    g_err[0] = '\0';
+    if (int st = naive_check(dtype, B, H, N)) return st;
+    if (causal != 0 && causal != 1) return fail(FA_ERR_ARG, "causal must be 0 or 1, got %d", causal);
+    const long long BH = static_cast<long long>(B) * H;
+    if (BH == 0 || N == 0) return FA_OK;
+    if (!s || !p) return fail(FA_ERR_NULL, "s and p must be non-NULL");
+    if (misaligned(s) || misaligned(p) || misaligned(lse)) return fail(FA_ERR_ALIGN, "s, p and lse must be 16-byte aligned");
+    const size_t cells = static_cast<size_t>(BH) * N * naive_ld(N);
+    if (overlaps(p, cells * 2, s, cells * 4)) return fail(FA_ERR_ARG, "p must not overlap s");
+    if (lse && (overlaps(lse, static_cast<size_t>(BH) * N * 4, s, cells * 4) ||
+                overlaps(lse, static_cast<size_t>(BH) * N * 4, p, cells * 2)))
+        return fail(FA_ERR_ARG, "lse must not overlap s or p");
+    return from_hip(fa::launch_naive_softmax_16(dtype == FA_BF16, s, p, lse, static_cast<int>(BH), N,
+                                                static_cast<int>(naive_ld(N)), causal != 0,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                    "fa_naive_softmax");
+}
+
+int fa_naive_pv(const void* p, const void* v, void* o, int B, int H, int N, int d, int dtype, void* stream) {
+    g_err[0] = '\0';
+    if (int st = naive_check(dtype, B, H, N)) return st;
+    if (d != 64 && d != 128 && d != 256) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128, 256)", d);
+    const long long BH = static_cast<long long>(B) * H;
+    if (BH == 0 || N == 0) return FA_OK;
+    if (!p || !v || !o) return fail(FA_ERR_NULL, "p, v and o must be non-NULL");
+    if (misaligned(p) || misaligned(v) || misaligned(o)) return fail(FA_ERR_ALIGN, "p, v and o must be 16-byte aligned");
+    const size_t ob = static_cast<size_t>(BH) * N * d * 2, pb = static_cast<size_t>(BH) * N * naive_ld(N) * 2;
+    if (overlaps(o, ob, p, pb) || overlaps(o, ob, v, ob)) return fail(FA_ERR_ARG, "o must not overlap p or v");
+    return from_hip(fa::launch_naive_pv_16(dtype == FA_BF16, p, v, o, static_cast<int>(BH), N, d,
+                                           static_cast<int>(naive_ld(N)), reinterpret_cast<hipStream_t>(stream)),
+                    "fa_naive_pv");
+}
+
+int fa_fwd_naive(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                 int causal, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    if (int st = naive_check(dtype, B, H, N)) return st;
+    if (causal != 0 && causal != 1) return fail(FA_ERR_ARG, "causal must be 0 or 1, got %d", causal);
+    if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale must be finite");
+    if (d != 64 && d != 128 && d != 256) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128, 256)", d);
+    const long long BH = static_cast<long long>(B) * H;
+    if (BH == 0 || N == 0) return FA_OK;
+    if (!q || !k || !v || !o || !workspace) return fail(FA_ERR_NULL, "q, k, v, o and workspace must be non-NULL");
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) || misaligned(workspace))
+        return fail(FA_ERR_ALIGN, "q, k, v, o, lse and workspace must be 16-byte aligned");
+    const size_t need = fa_naive_workspace_bytes(B, H, N);
+    if (workspace_bytes < need) return fail(FA_ERR_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    const size_t tb = static_cast<size_t>(BH) * N * d * 2;
+    if (overlaps(o, tb, q, tb) || overlaps(o, tb, k, tb) || overlaps(o, tb, v, tb))
+        return fail(FA_ERR_ARG, "o must not overlap q, k or v");
+    if (overlaps(workspace, need, q, tb) || overlaps(workspace, need, k, tb) || overlaps(workspace, need, v, tb) ||
+        overlaps(workspace, need, o, tb) || (lse && overlaps(workspace, need, lse, static_cast<size_t>(BH) * N * 4)))
+        return fail(FA_ERR_ARG, "workspace must not overlap any tensor");
+    if (lse && overlaps(lse, static_cast<size_t>(BH) * N * 4, o, tb)) return fail(FA_ERR_ARG, "lse must not overlap o");
+    float* s = static_cast<float*>(workspace);
+    char* p = static_cast<char*>(workspace) + static_cast<size_t>(BH) * N * naive_ld(N) * 4;
+    if (int st = fa_naive_scores(q, k, s, B, H, N, d, scale, dtype, stream)) return st;
+    if (int st = fa_naive_softmax(s, p, lse, B, H, N, causal, dtype, stream)) return st;
+    return fa_naive_pv(p, v, o, B, H, N, d, dtype, stream);
 }
 
 int fa_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, const int8_t* hadamard, int block, int BH, int N,

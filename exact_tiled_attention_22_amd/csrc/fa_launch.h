@@ -40,4 +40,13 @@ hipError_t launch_decode_16(bool is_bf16, const void* q, const void* k, const vo
                             int BH, int Nq, int Nk, int d, bool causal, int nsplit, int chunk, float c, uint32_t qflip,
                             hipStream_t stream);
 
+// unfused attention (bf16 / fp16, d in {64, 128, 256}): S = scale Q K^T as float32 [BH, N, ld]; P = softmax(S)
+// in the input dtype [BH, N, ld] (zero on the padding columns) with lse; O = P V.  ld = N rounded up to 64.
+hipError_t launch_naive_scores_16(bool is_bf16, const void* q, const void* k, float* s, int BH, int N, int d, int ld,
+                                  float scale, hipStream_t stream);
+hipError_t launch_naive_softmax_16(bool is_bf16, const float* s, void* p, float* lse, int BH, int N, int ld, bool causal,
+                                   hipStream_t stream);
+hipError_t launch_naive_pv_16(bool is_bf16, const void* p, const void* v, void* o, int BH, int N, int d, int ld,
+                              hipStream_t stream);
+
 }  // namespace fa

@@ -157,6 +157,35 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* dq, void* dk, void* dv, float* delta,
            int B, int H, int N, int d, int causal, float scale, int dtype, void* stream);
 
+/*
+ * Unfused attention: the standard implementation that the tiled method is measured against (concept
+ * card "FlashAttention 2 + 3 — speicherbewusste Attention-Kernels", "Worum es geht" and "Kernpunkte":
+ * the classic path writes the full score matrix to HBM and reads it back; Flash Attention glossary,
+ * "/02 Technische Vorteile im Überblick": the speed-up over that path).  Same definition and outputs
+ * as fa_fwd, computed in three launches with the N x N matrices in device memory:
+ *   fa_naive_scores  : s = scale q k^T, float32 [B*H, N, ld], columns >= N of each row untouched.
+ *   fa_naive_softmax : p = softmax(s [+ causal mask, key j visible to query i iff j <= i]) per row, of
+ *                      type `dtype`, [B*H, N, ld], written as 0 on the masked and padding columns;
+ *                      lse [B,H,N] float32 (natural log, may be NULL).  float32 arithmetic, p rounded
+ *                      to nearest even.
+ *   fa_naive_pv      : o = p v, [B,H,N,d] of type `dtype`, float32 accumulation.
+ *   fa_fwd_naive     : the three in order, with s and p placed in `workspace`.
+ * ld = fa_naive_row_stride(N) = N rounded up to a multiple of 64 (elements).  q, k, v, o are DEVICE
+ * [B,H,N,d] of type `dtype` (FA_F16 or FA_BF16); d is 64, 128 or 256.  Every pointer is a caller-owned
+ * DEVICE pointer, 16-byte aligned; outputs overlap no input.  The causal mask is applied in the
+ * softmax only (every score is computed).  workspace: at least fa_naive_workspace_bytes(B, H, N)
+ * bytes (B*H*N*ld*6: s, then p); its contents on return are s and p.  Returns an fa_status.
+ */
+int fa_naive_row_stride(int N);
+size_t fa_naive_workspace_bytes(int B, int H, int N);
+int fa_naive_scores(const void* q, const void* k, float* s, int B, int H, int N, int d, float scale, int dtype,
+                    void* stream);
+int fa_naive_softmax(const float* s, void* p, float* lse, int B, int H, int N, int causal, int dtype, void* stream);
+int fa_naive_pv(const void* p, const void* v, void* o, int B, int H, int N, int d, int dtype, void* stream);
+int fa_fwd_naive(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, int causal, float scale, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* fa_status_str(int status);
 

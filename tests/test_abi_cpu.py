@@ -44,7 +44,9 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_fwd_decode", "fa_decode_workspace_bytes",
-                          "fa_fp8_prep", "fa_status_str", "fa_last_error", "fa_abi_version"}
+                          "fa_fp8_prep", "fa_status_str", "fa_last_error", "fa_abi_version",
+                          "fa_naive_row_stride", "fa_naive_workspace_bytes", "fa_naive_scores",
+                          "fa_naive_softmax", "fa_naive_pv", "fa_fwd_naive"}
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -164,3 +166,54 @@ def test_decode_validation_statuses(lib):
     assert call(work=p[1]) == FA_ERR_ARG  # workspace overlaps k
     assert call(pp=[p[0], p[1], p[2], p[0], p[4]]) == FA_ERR_ARG  # o aliases q
     assert call(Nq=0) == FA_OK
+
+
+def test_naive_validation_statuses(lib):
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.fa_naive_row_stride.argtypes = [ci]
+    lib.fa_naive_row_stride.restype = ci
+    lib.fa_naive_workspace_bytes.argtypes = [ci] * 3
+    lib.fa_naive_workspace_bytes.restype = ctypes.c_size_t
+    assert [lib.fa_naive_row_stride(n) for n in (1, 63, 64, 65, 1000)] == [64, 64, 64, 128, 1024]
+    assert lib.fa_naive_workspace_bytes(2, 3, 100) == 2 * 3 * 100 * 128 * 6
+    assert lib.fa_naive_workspace_bytes(0, 3, 100) == 0
+    f = lib.fa_fwd_naive
+    f.argtypes = [vp] * 5 + [ci] * 5 + [ctypes.c_float, ci, vp, ctypes.c_size_t, vp]
+    f.restype = ci
+    need = lib.fa_naive_workspace_bytes(2, 4, 100)
+    big = 1 << 26
+    p = [big * (i + 1) for i in range(5)]  # q k v o lse
+    w = big * 8
+
+    def call(pp=None, B=2, H=4, N=100, d=128, causal=0, scale=0.1, dtype=2, work=w, nbytes=None):
+        return f(*(pp or p), B, H, N, d, causal, scale, dtype, work, need if nbytes is None else nbytes, None)
+
+    # every call below fails validation (or is empty): nothing is launched on these fake pointers
+    assert call(dtype=0) == FA_ERR_UNSUPPORTED
+    assert call(dtype=3) == FA_ERR_UNSUPPORTED
+    assert call(dtype=9) == FA_ERR_DTYPE
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(N=-1) == FA_ERR_SHAPE
+    assert call(causal=3) == FA_ERR_ARG
+    assert call(scale=float("nan")) == FA_ERR_ARG
+    assert call(nbytes=need - 1) == FA_ERR_ARG
+    assert call(work=None) == FA_ERR_NULL
+    assert call(work=w + 4) == FA_ERR_ALIGN
+    assert call(work=p[2]) == FA_ERR_ARG  # workspace overlaps v
+    assert call(pp=[p[0], p[1], p[2], p[2], p[4]]) == FA_ERR_ARG  # o aliases v
+    assert call(N=0) == FA_OK
+    sc = lib.fa_naive_scores
+    sc.argtypes = [vp, vp, vp, ci, ci, ci, ci, ctypes.c_float, ci, vp]
+    sc.restype = ci
+    assert sc(p[0], p[1], p[0], 2, 4, 100, 128, 0.1, 2, None) == FA_ERR_ARG  # s overlaps q
+    assert sc(p[0], None, w, 2, 4, 100, 128, 0.1, 2, None) == FA_ERR_NULL
+    sm = lib.fa_naive_softmax
+    sm.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp]
+    sm.restype = ci
+    assert sm(w, w + 64, None, 2, 4, 100, 0, 2, None) == FA_ERR_ARG  # p overlaps s
+    assert sm(w, p[0], None, 2, 4, 100, 2, 2, None) == FA_ERR_ARG  # causal = 2
+    pv = lib.fa_naive_pv
+    pv.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp]
+    pv.restype = ci
+    assert pv(w, p[2], p[2], 2, 4, 100, 128, 2, None) == FA_ERR_ARG  # o aliases v
+    assert pv(w, p[2], p[3], 2, 4, 100, 64 + 1, 2, None) == FA_ERR_UNSUPPORTED
