@@ -11,6 +11,8 @@ What it computes, in float64 on the CPU, straight from the definitions:
   The pages say the tiled method returns the same output as this plain softmax formula
   (FlashAttention 2 + 3 — speicherbewusste Attention-Kernels, "Kernpunkte" and "Worum es geht";
   Flash Attention glossary, "/01 Was ist Flash Attention?").
+* ``attention_probs`` — the score and probability matrices of one head, as the unfused comparison path
+  holds them in memory.
 * ``attention_rect`` — the same definition for Nq queries against Nk >= Nq cached keys (the decode
   shape), with the causal mask aligned to the end of the key sequence.
 * ``attention_bwd_ref`` / ``attention_bwd_rows`` — the gradients dQ, dK, dV of that definition for a
@@ -28,7 +30,14 @@ per-row score shift), and torch's float8_e4m3fn conversion for the codec.  No fu
 "parity unpinned".
 """
 
-from .attention import attention_bwd_ref, attention_bwd_rows, attention_rect, attention_ref, attention_rows  # noqa: F401
+from .attention import (  # noqa: F401
+    attention_bwd_ref,
+    attention_bwd_rows,
+    attention_probs,
+    attention_rect,
+    attention_ref,
+    attention_rows,
+)
 from .fp8 import (  # noqa: F401
     E4M3_MAX,
     dequantize_blocks,

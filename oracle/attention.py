@@ -132,3 +132,18 @@ def attention_rect(qh, kh, vh, causal: bool, scale: float):
     e = np.exp(s - m)
     l = e.sum(axis=1, keepdims=True)
     return (e @ vh) / l, m[:, 0] + np.log(l[:, 0])
+
+
+def attention_probs(qh, kh, causal: bool, scale: float):
+    """The intermediate matrices of the definition for ONE head, as the standard (unfused) implementation
+    materialises them: scores s = scale Q K^T [N, N] (all entries, mask not applied), probabilities
+    P_ij = exp(s_ij - m_i) / l_i on the visible keys and 0 elsewhere, and lse [N].  float64, full rows
+    (concept card "Worum es geht": the classic path holds the whole score matrix)."""
+    qh, kh = _f64(qh), _f64(kh)
+    n = qh.shape[0]
+    s = float(scale) * (qh @ kh.T)
+    sm = np.where(np.arange(n)[None, :] <= np.arange(n)[:, None], s, -np.inf) if causal else s
+    m = sm.max(axis=1, keepdims=True)
+    e = np.exp(sm - m)
+    l = e.sum(axis=1, keepdims=True)
+    return s, e / l, m[:, 0] + np.log(l[:, 0])
