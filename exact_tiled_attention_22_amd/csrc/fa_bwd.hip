@@ -11,8 +11,8 @@
 //   1. delta_kernel: D = rowsum(dO o O), float32 [B,H,N] in a caller-provided buffer;
 //   2. BwdQ: one workgroup per 128 query rows streams the K/V tiles (as the forward pass does) and
 //      accumulates dQ^T = K^T dS^T in registers;
-//   3. BwdKV: one workgroup per 128 keys streams the Q/dO tiles (with their lse and D) and
-//      accumulates dV^T = dO^T P and dK^T = Q^T dS in registers.
+//   3. BwdKV: one workgroup per 128 keys (V rows held in LDS, K rows in registers) streams the Q/dO
+//      tiles (with their lse and D) and accumulates dV^T = dO^T P and dK^T = Q^T dS in registers.
 // Operand conventions are the forward pass's: v_mfma_f32_32x32x16 with the A-operand rows permuted
 // so that 8 consecutive accumulator registers of a lane hold 8 consecutive rows (keys in BwdQ,
 // queries in BwdKV), which lets P and dS feed the next MFMA as its B operand in place, and
@@ -226,18 +226,23 @@ struct BwdQ {
 };
 
 // ---------------------------------------------------------------------------------------------
-// dK, dV: one workgroup = 4 waves x 32 keys; query tiles of 64 rows (Q, dO, lse, D) through two
-// LDS stages.  Per stage: Q tile | dO tile | lse * log2(e) [64] | D [64].
+// dK, dV: one workgroup = 4 waves x 32 keys.  The workgroup's 128 V rows stay in LDS for the whole
+// kernel (B operand of dP = dO V^T); the K rows of a wave stay in its registers (B operand of
+// S = Q K^T).  Query tiles of 32 rows (Q, dO, lse, D) stream through two LDS stages.  This keeps a
+// wave under 256 registers and the workgroup at 64.5 KiB of LDS, so two workgroups share a CU and
+// one's MFMAs overlap the other's exponentials.  LDS: V [128 rows] | stage 0 | stage 1, a stage
+// being Q tile | dO tile | lse * log2(e) [32] | D [32].
 template <typename T, int D, bool CAUSAL>
 struct BwdKV {
     using VT = Vec<T>;
     using x8 = typename VT::x8;
     using x4 = typename VT::x4;
-    static constexpr int NW = 4, THREADS = 256, KW = 32, BK = NW * KW, BQ = 64;
+    static constexpr int NW = 4, THREADS = 256, KW = 32, BK = NW * KW, BQ = 32;
     static constexpr int CPR = D / 8, KS = D / 16, CB = D / 32;
     static constexpr int TILE = BQ * CPR * 16;
+    static constexpr int VBYTES = BK * CPR * 16;
     static constexpr int STAGE = 2 * TILE + 2 * BQ * 4;
-    static constexpr int LDS_BYTES = 2 * STAGE;
+    static constexpr int LDS_BYTES = VBYTES + 2 * STAGE;
 
     static __device__ __forceinline__ void run(const T* __restrict__ Q, const T* __restrict__ K,
                                                const T* __restrict__ V, const T* __restrict__ dO,
@@ -259,26 +264,25 @@ struct BwdKV {
         const int t0 = CAUSAL ? k0 / BQ : 0;        // first query tile with a visible key of the workgroup
         const int t0w = CAUSAL ? kw0 / BQ : 0;      // ... of this wave
         const Geo<CPR> g(lane);
+        const int vrow = wave * KW + n32;           // this lane's V row in LDS
 
-        // B operands of S = Q K^T and dP = dO V^T: this lane's key row, 8 columns per k-step
-        x8 kreg[KS], vreg[KS];
+        // B operand of S = Q K^T: this lane's key row, 8 columns per k-step
+        x8 kreg[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            kreg[ks] = *(const x8*)(K + head + (size_t)krow * D + ks * 16 + h * 8);
-            vreg[ks] = *(const x8*)(V + head + (size_t)krow * D + ks * 16 + h * 8);
-        }
+        for (int ks = 0; ks < KS; ++ks) kreg[ks] = *(const x8*)(K + head + (size_t)krow * D + ks * 16 + h * 8);
         // lse and D of a query tile: wave 0 loads lse, wave 1 loads D, one row per lane (clamped)
         auto load_ld = [&](int tq) -> float {
-            const int r = min(tq * BQ + lane, N - 1);
+            const int r = min(tq * BQ + (lane & (BQ - 1)), N - 1);
             return wave == 0 ? lseh[r] * kLog2e : dlh[r];
         };
         auto issue = [&](int tq, uint32_t st) {
             copy_tile<T, D, BQ, THREADS>(Q + head, tq * BQ, N, lbase + st, tid, wave);
             copy_tile<T, D, BQ, THREADS>(dO + head, tq * BQ, N, lbase + st + TILE, tid, wave);
         };
+        copy_tile<T, D, BK, THREADS>(V + head, k0, N, lbase, tid, wave);
         float ldv = 0.0f;
         if (t0 < ntq) {
-            issue(t0, 0);
+            issue(t0, VBYTES);
             if (wave < 2) ldv = load_ld(t0);
         }
 
@@ -288,7 +292,7 @@ struct BwdKV {
 
         auto iteration = [&](int tq, uint32_t cur, uint32_t nxt) {
             wait_vmcnt<0>();
-            if (wave < 2) *(float*)(smem + cur + 2 * TILE + wave * BQ * 4 + lane * 4) = ldv;
+            if (wave < 2 && lane < BQ) *(float*)(smem + cur + 2 * TILE + wave * BQ * 4 + lane * 4) = ldv;
             lds_barrier();
             if (tq + 1 < ntq) {
                 issue(tq + 1, nxt);
@@ -299,46 +303,41 @@ struct BwdKV {
             const char* gl = smem + cur + TILE;
             const float* lsl = (const float*)(smem + cur + 2 * TILE);
             const float* dsl = lsl + BQ;
-            f32x16 s[2], dp[2];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) s[qb] = dp[qb] = f32x16{};
+            f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    s[qb] = VT::mfma(*(const x8*)(ql + g.aoff(qb, ks)), kreg[ks], s[qb]);
-                    dp[qb] = VT::mfma(*(const x8*)(gl + g.aoff(qb, ks)), vreg[ks], dp[qb]);
-                }
+                const x8 vop = *(const x8*)(smem + (vrow * CPR + ((2 * ks + g.h) ^ bswz<CPR>(vrow))) * 16);
+                s = VT::mfma(*(const x8*)(ql + g.aoff(0, ks)), kreg[ks], s);
+                dp = VT::mfma(*(const x8*)(gl + g.aoff(0, ks)), vop, dp);
             }
-            // register r of query block qb holds query qb*32 + (r/8)*16 + h*8 + r%8 (of the tile)
-            x8 pb[4], dsb[4];
+            // register r holds query (r/8)*16 + h*8 + r%8 of the tile, key `key`
+            x8 pb[2], dsb[2];
             const bool edge = (tq * BQ + BQ > N) || (CAUSAL && kw0 + KW - 1 > tq * BQ);
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const int qb = st >> 1, hf = st & 1;
-                const int qi = qb * 32 + hf * 16 + h * 8;  // first of the 8 queries
+            for (int st = 0; st < 2; ++st) {
+                const int qi = st * 16 + h * 8;  // first of the 8 queries
                 const f32x4 l0 = *(const f32x4*)(lsl + qi), l1 = *(const f32x4*)(lsl + qi + 4);
                 const f32x4 d0 = *(const f32x4*)(dsl + qi), d1 = *(const f32x4*)(dsl + qi + 4);
                 float pv[8], dv8[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int r = hf * 8 + e;
+                    const int r = st * 8 + e;
                     const float l2 = e < 4 ? l0[e] : l1[e - 4];
                     const float de = e < 4 ? d0[e] : d1[e - 4];
-                    float p = fast_exp2(__builtin_fmaf(s[qb][r], c, -l2));
+                    float p = fast_exp2(__builtin_fmaf(s[r], c, -l2));
                     if (edge) {
                         const int qq = tq * BQ + qi + e;
                         if (qq >= N || (CAUSAL && key > qq)) p = 0.0f;
                     }
                     pv[e] = p;
-                    dv8[e] = p * (dp[qb][r] - de);
+                    dv8[e] = p * (dp[r] - de);
                 }
                 pb[st] = VT::pack(pv);
                 dsb[st] = VT::pack(dv8);
             }
-            // dV^T += dO^T P, dK^T += Q^T dS over the tile's four 16-query steps
+            // dV^T += dO^T P, dK^T += Q^T dS over the tile's two 16-query steps
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
+            for (int st = 0; st < 2; ++st) {
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
                     const x4 glo = VT::read_tr(gl + g.toff(cb, st, 0));
@@ -351,8 +350,8 @@ struct BwdKV {
             }
         };
         for (int tq = t0; tq < ntq; tq += 2) {
-            iteration(tq, 0, STAGE);
-            if (tq + 1 < ntq) iteration(tq + 1, STAGE, 0);
+            iteration(tq, VBYTES, VBYTES + STAGE);
+            if (tq + 1 < ntq) iteration(tq + 1, VBYTES + STAGE, VBYTES);
         }
         if (key < N) {
             T* krw = dK + head + (size_t)key * D;
@@ -385,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(const T* __restrict__ Q, 
 }
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256, 2) void bwd_kv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                         const T* __restrict__ V, const T* __restrict__ dO,
                                                         const float* __restrict__ LSE, const float* __restrict__ Dl,
                                                         T* __restrict__ dK, T* __restrict__ dV, int N, int BH,
