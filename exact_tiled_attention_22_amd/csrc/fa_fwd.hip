@@ -12,9 +12,9 @@
 // Work layout (one workgroup = NW waves = BM = NW * 32 * QB query rows of one (b, h)):
 //   * each wave owns QB blocks of 32 query rows; its Q operand is loaded once from HBM straight into
 //     registers (together with the first K/V copies, so the prologue pays one memory latency);
-//   * key/value tiles of BN = 64 rows stream through two LDS stages each; K runs one tile ahead of V:
-//     during iteration j the LDS holds K_{j+1} and V_j while K_{j+2} and V_{j+1} are copied in, so
-//     one barrier per tile suffices;
+//   * key/value tiles of BN = 64 rows (32 for d = 256) stream through two LDS stages each; for
+//     d <= 128 K runs one tile ahead of V: during iteration j the LDS holds K_{j+1} and V_j while
+//     K_{j+2} and V_{j+1} are copied in, so one barrier per tile suffices;
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: lane l holds the scores
 //     of query (l % 32) for 16 keys of each 32-key block, so the row maximum and sum are in-lane plus
 //     one exchange between the two wave halves;
@@ -34,7 +34,8 @@ constexpr float kTau = 8.0f;  // rescale only when the running maximum grows by 
 
 template <int D, int QB, int NW, int WPC>
 struct Tile {
-    static constexpr int BN = 64;                 // keys per tile
+    // keys per tile: 64, or 32 for d = 256 so that two workgroups (two waves per SIMD) fit a CU
+    static constexpr int BN = D >= 256 ? 32 : 64;
     static constexpr int QW = 32 * QB;            // query rows per wave
     static constexpr int BM = QW * NW;            // query rows per workgroup
     static constexpr int THREADS = 64 * NW;
@@ -42,18 +43,12 @@ struct Tile {
     static constexpr int CHUNKS = BN * CPR;       // chunks per K (or V) tile
     static constexpr int LPT = CHUNKS / THREADS;  // direct-to-LDS copies per thread per tile
     static constexpr int KV_BYTES = CHUNKS * 16;
-    static constexpr int Q_CHUNKS = BM * CPR;
-    static constexpr int QLPT = Q_CHUNKS / THREADS;
-    static constexpr int Q_BYTES = Q_CHUNKS * 16;
-    // WPC workgroups share a CU's 160 KiB of LDS: two K stages and two V stages.  The in-order
-    // pipeline stages Q through stage 1 (K1|V1) during its prologue; the K-ahead pipeline loads Q
+    // WPC workgroups share a CU's 160 KiB of LDS: two K stages and two V stages.  Q goes from HBM
     // straight into registers.
     static constexpr int LDS_LIMIT = 160 * 1024 / WPC;
     static constexpr int LDS_BYTES = 4 * KV_BYTES;
     static constexpr int OFF_K0 = 0, OFF_V0 = KV_BYTES, OFF_K1 = 2 * KV_BYTES, OFF_V1 = 3 * KV_BYTES;
-    static constexpr int OFF_Q = OFF_K1;
-    static_assert(CHUNKS % THREADS == 0 && Q_CHUNKS % THREADS == 0, "tiles split evenly over threads");
-    static_assert(Q_BYTES <= 2 * KV_BYTES, "Q staging must fit in stage 1");
+    static_assert(CHUNKS % THREADS == 0, "tiles split evenly over threads");
     static_assert(LDS_BYTES <= LDS_LIMIT, "LDS budget");
     static_assert(LPT <= 16, "vmcnt range");
 };
@@ -81,35 +76,25 @@ struct Fwd {
     static constexpr int KS = D / 16;  // k-steps of the score product
     static constexpr int CB = D / 32;  // 32-column blocks of the output
     static constexpr int OFF_K0 = TL::OFF_K0, OFF_V0 = TL::OFF_V0, OFF_K1 = TL::OFF_K1, OFF_V1 = TL::OFF_V1;
-    static constexpr int OFF_Q = TL::OFF_Q;
+    static constexpr int NKB = BN / 32;  // 32-key blocks per tile
 
     // Copy rows [r0, r0 + ROWS) of a [N, D] slice into an LDS tile, ROWS = NLOADS * THREADS / CPR.
-    // Slot s of the tile holds chunk (s % CPR) ^ swz(row) of row s / CPR.  When every row exists the
-    // copies use a scalar tile base and per-lane 32-bit offsets; a ragged last tile reads row N-1 in
-    // place of the missing rows (they are masked or never stored).
+    // Slot s of the tile holds chunk (s % CPR) ^ swz(row) of row s / CPR.  The copies use a scalar
+    // tile base and per-lane 32-bit offsets; a ragged last tile reads row N-1 in place of the missing
+    // rows (they are masked or never stored), through a wave-uniform row limit.
     template <int NLOADS>
     static __device__ __forceinline__ void copy_rows(const T* __restrict__ src, int r0, int N, uint32_t lds,
                                                      int tid, int wave) {
         constexpr int ROWS = NLOADS * TL::THREADS / CPR;
-        if (r0 + ROWS <= N) {
-            const T* base = src + (size_t)r0 * D;
+        const T* base = src + (size_t)r0 * D;
+        const int lim = min(ROWS, N - r0) - 1;  // last row of the slice inside this tile
 #pragma unroll
-            for (int t = 0; t < NLOADS; ++t) {
-                const int slot = t * TL::THREADS + tid;
-                const int row = slot / CPR;
-                const int c = (slot % CPR) ^ swz<CPR>(row);
-                dma16s(base, (uint32_t)((row * D + c * 8) * (int)sizeof(T)),
-                       lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < NLOADS; ++t) {
-                const int slot = t * TL::THREADS + tid;
-                const int row = slot / CPR;
-                const int c = (slot % CPR) ^ swz<CPR>(row);
-                const T* g = src + (size_t)min(r0 + row, N - 1) * D + c * 8;
-                dma16(g, lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
-            }
+        for (int t = 0; t < NLOADS; ++t) {
+            const int slot = t * TL::THREADS + tid;
+            const int row = slot / CPR;
+            const int c = (slot % CPR) ^ swz<CPR>(row);
+            dma16s(base, (uint32_t)((min(row, lim) * D + c * 8) * (int)sizeof(T)),
+                   lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
         }
     }
 
@@ -126,18 +111,18 @@ struct Fwd {
         }
     };
 
-    // S^T = K_tile Q^T for this wave's QB query blocks (fp32 accumulate).  The second 32-key block
+    // S^T = K_tile Q^T for this wave's QB query blocks (fp32 accumulate).  A second 32-key block
     // sits 32 rows further (a compile-time offset).
-    static __device__ __forceinline__ void scores(const char* kl, const x8 (&qreg)[QB][KS], f32x16 (&s)[QB][2],
+    static __device__ __forceinline__ void scores(const char* kl, const x8 (&qreg)[QB][KS], f32x16 (&s)[QB][NKB],
                                                   const Lane& ln) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) s[qb][kb] = f32x16{};
+            for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < NKB; ++kb) {
                 const x8 kop = *(const x8*)(kl + ln.koff(ks) + kb * 32 * CPR * 16);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) s[qb][kb] = VT::mfma(kop, qreg[qb][ks], s[qb][kb]);
@@ -146,13 +131,13 @@ struct Fwd {
     }
 
     // Hide keys past N and (causal) keys after the query; true when the tile needs it.
-    static __device__ __forceinline__ void mask(f32x16 (&s)[QB][2], int kv0, int N, int q0w, int n32, int h) {
+    static __device__ __forceinline__ void mask(f32x16 (&s)[QB][NKB], int kv0, int N, int q0w, int n32, int h) {
         if ((kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > q0w)) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const int query = q0w + qb * 32 + n32;
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kv0 + kb * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
@@ -164,23 +149,31 @@ struct Fwd {
 
     // Running maximum in base-2 units; the accumulator and sum are rescaled only when some row's
     // maximum grew by more than 2^tau (p = 2^(s*c - m) then stays <= 2^tau, exact either way).
-    static __device__ __forceinline__ void update_max(const f32x16 (&s)[QB][2], float c, f32x16 (&oacc)[QB][CB],
+    static __device__ __forceinline__ void update_max(const f32x16 (&s)[QB][NKB], float c, f32x16 (&oacc)[QB][CB],
                                                       float (&m_run)[QB], float (&l_run)[QB]) {
         float mt[QB];
         bool grow = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            // 32 values -> 1 as a shallow tree of 3-input maxima (short dependency chain)
-            float t1[11];
+            // 16 NKB values -> 1 as a shallow tree of 3-input maxima (short dependency chain)
+            float mx;
+            if constexpr (NKB == 2) {
+                float t1[11];
 #pragma unroll
-            for (int i = 0; i < 10; ++i) {
-                const int a = 3 * i, b = 3 * i + 1, d = 3 * i + 2;
-                t1[i] = fmaxf(fmaxf(s[qb][a >> 4][a & 15], s[qb][b >> 4][b & 15]), s[qb][d >> 4][d & 15]);
+                for (int i = 0; i < 10; ++i) {
+                    const int a = 3 * i, b = 3 * i + 1, d = 3 * i + 2;
+                    t1[i] = fmaxf(fmaxf(s[qb][a >> 4][a & 15], s[qb][b >> 4][b & 15]), s[qb][d >> 4][d & 15]);
+                }
+                t1[10] = fmaxf(s[qb][1][14], s[qb][1][15]);
+                const float t2a = fmaxf(fmaxf(t1[0], t1[1]), t1[2]), t2b = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
+                const float t2c = fmaxf(fmaxf(t1[6], t1[7]), t1[8]), t2d = fmaxf(t1[9], t1[10]);
+                mx = fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d));
+            } else {
+                float t1[5];
+#pragma unroll
+                for (int i = 0; i < 5; ++i) t1[i] = fmaxf(fmaxf(s[qb][0][3 * i], s[qb][0][3 * i + 1]), s[qb][0][3 * i + 2]);
+                mx = fmaxf(fmaxf(fmaxf(t1[0], t1[1]), t1[2]), fmaxf(fmaxf(t1[3], t1[4]), s[qb][0][15]));
             }
-            t1[10] = fmaxf(s[qb][1][14], s[qb][1][15]);
-            const float t2a = fmaxf(fmaxf(t1[0], t1[1]), t1[2]), t2b = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
-            const float t2c = fmaxf(fmaxf(t1[6], t1[7]), t1[8]), t2d = fmaxf(t1[9], t1[10]);
-            const float mx = fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d));
             mt[qb] = halves_max(mx) * c;
             grow |= mt[qb] > m_run[qb] + kTau;
         }
@@ -198,14 +191,14 @@ struct Fwd {
     }
 
     // P = 2^(s*c - m) rounded to T (row sums from the fp32 values)
-    static __device__ __forceinline__ void exps(const f32x16 (&s)[QB][2], float c, const float (&m_run)[QB],
-                                                float (&l_run)[QB], x8 (&p)[QB][4]) {
+    static __device__ __forceinline__ void exps(const f32x16 (&s)[QB][NKB], float c, const float (&m_run)[QB],
+                                                float (&l_run)[QB], x8 (&p)[QB][2 * NKB]) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const float negm = -m_run[qb];
-            float part[4];
+            float part[2 * NKB];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < NKB; ++kb) {
                 float e[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) e[r] = fast_exp2(__builtin_fmaf(s[qb][kb][r], c, negm));
@@ -217,16 +210,17 @@ struct Fwd {
                     part[kb * 2 + hf] = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
                 }
             }
-            l_run[qb] += (part[0] + part[1]) + (part[2] + part[3]);
+            if constexpr (NKB == 2) l_run[qb] += (part[0] + part[1]) + (part[2] + part[3]);
+            else l_run[qb] += part[0] + part[1];
         }
     }
 
     // O^T += V^T P^T for one tile (V^T operands through transposing LDS reads); 16-key step s sits
     // 16 rows further (a compile-time offset).
-    static __device__ __forceinline__ void pv(const char* vl, const x8 (&p)[QB][4], f32x16 (&oacc)[QB][CB],
+    static __device__ __forceinline__ void pv(const char* vl, const x8 (&p)[QB][2 * NKB], f32x16 (&oacc)[QB][CB],
                                               const Lane& ln) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 2 * NKB; ++s) {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 const x4 lo = VT::read_tr(vl + ln.voff(cb, 0) + s * 16 * CPR * 16);
@@ -242,7 +236,7 @@ struct Fwd {
     // run a few ahead of the score MFMAs, each score MFMA is followed by softmax VALU work (which does
     // not depend on it), then the V operand reads run ahead of the value MFMAs.
     static __device__ __forceinline__ void interleave() {
-        constexpr int NQK = KS * 2 * QB, NKR = KS * 2, NPV = 4 * CB * QB;
+        constexpr int NQK = KS * NKB * QB, NKR = KS * NKB, NPV = 2 * NKB * CB * QB;
         constexpr int AHEAD = D >= 256 ? 2 : 4;
         __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // first K reads
 #pragma unroll
@@ -290,8 +284,7 @@ struct Fwd {
 
     // In-order pipeline for large head dimensions (one score buffer): iteration j holds K_j and V_j
     // in stage j % 2 and copies K_{j+1}, V_{j+1} into the other stage; the scores of tile j come first,
-    // then its softmax, whose exponentials interleave with the value MFMAs.  Q is staged through
-    // stage 1 during the prologue.
+    // then its softmax, whose exponentials interleave with the value MFMAs.
     static __device__ __forceinline__ void run_seq(const T* __restrict__ Q, const T* __restrict__ K,
                                                    const T* __restrict__ V, T* __restrict__ O,
                                                    float* __restrict__ LSE, int N, int BH, int ntq, float c,
@@ -321,24 +314,20 @@ struct Fwd {
             ln.vcc = (G & 1) * 2 + ((i16 & 3) >> 1);
             ln.vb = (i16 & 1) * 8;
         }
-        copy_rows<TL::QLPT>(Qh, q0, N, lbase + OFF_Q, tid, wave);
-        copy_rows<LPT>(Kh, 0, N, lbase + OFF_K0, tid, wave);
-        copy_rows<LPT>(Vh, 0, N, lbase + OFF_V0, tid, wave);
-        wait_vmcnt<0>();
-        lds_barrier();
+        // Q operand straight from HBM (the first iteration's wait covers these loads and the copies)
         x8 qreg[QB][KS];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const int row = wave * QW + qb * 32 + n32;
-            const char* qrow = smem + OFF_Q + row * CPR * 16;
-            const int qsw = swz<CPR>(row);
+            const T* src = Qh + (size_t)min(q0w + qb * 32 + n32, N - 1) * D + h * 8;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                i32x4 raw = *(const i32x4*)(qrow + ((2 * ks + h) ^ qsw) * 16);
+                i32x4 raw = *(const i32x4*)(src + ks * 16);
                 raw ^= (int)qflip;
                 qreg[qb][ks] = __builtin_bit_cast(x8, raw);
             }
         }
+        copy_rows<LPT>(Kh, 0, N, lbase + OFF_K0, tid, wave);
+        copy_rows<LPT>(Vh, 0, N, lbase + OFF_V0, tid, wave);
         f32x16 oacc[QB][CB];
         float m_run[QB], l_run[QB];
 #pragma unroll
@@ -350,17 +339,17 @@ struct Fwd {
         }
         auto iteration = [&](int j, int ok, int ov, uint32_t dk, uint32_t dv) {
             wait_vmcnt<0>();
-            lds_barrier();  // K_j, V_j visible; the other stage (and the Q staging) is free
+            lds_barrier();  // K_j, V_j visible; the other stage is free
             if (j + 1 < nt) {
                 copy_rows<LPT>(Kh, (j + 1) * BN, N, lbase + dk, tid, wave);
                 copy_rows<LPT>(Vh, (j + 1) * BN, N, lbase + dv, tid, wave);
             }
             if (j < ntw) {
-                f32x16 sc[QB][2];
+                f32x16 sc[QB][NKB];
                 scores(smem + ok, qreg, sc, ln);
                 mask(sc, j * BN, N, q0w, n32, h);
                 update_max(sc, c, oacc, m_run, l_run);
-                x8 p[QB][4];
+                x8 p[QB][2 * NKB];
                 exps(sc, c, m_run, l_run, p);
                 pv(smem + ov, p, oacc, ln);
             }
@@ -433,11 +422,11 @@ struct Fwd {
             for (int cb = 0; cb < CB; ++cb) oacc[qb][cb] = f32x16{};
         }
 
-        f32x16 s0[QB][2], s1[QB][2];
+        f32x16 s0[QB][NKB], s1[QB][NKB];
         scores(smem + OFF_K0, qreg, s0, ln);
 
         // ---- main loop: iteration j holds K_{j+1} and V_j, copies K_{j+2} and V_{j+1} ----
-        auto iteration = [&](int j, f32x16 (&cur)[QB][2], f32x16 (&nxt)[QB][2], int okn, int ov, uint32_t dk,
+        auto iteration = [&](int j, f32x16 (&cur)[QB][NKB], f32x16 (&nxt)[QB][NKB], int okn, int ov, uint32_t dk,
                              uint32_t dv) {
             wait_vmcnt<0>();
             lds_barrier();
@@ -454,7 +443,7 @@ struct Fwd {
                 // of competing with the matrix instructions
                 __builtin_amdgcn_s_setprio(1);
                 scores(smem + okn, qreg, nxt, ln);
-                x8 p[QB][4];
+                x8 p[QB][2 * NKB];
                 exps(cur, c, m_run, l_run, p);
                 pv(smem + ov, p, oacc, ln);
                 interleave();
@@ -488,7 +477,7 @@ __global__ __launch_bounds__(64 * NW, (NW * WPC) / 4) void fa_fwd16_kernel(
 template <int D> struct Shape;
 template <> struct Shape<64> { static constexpr int QB = 1, NW = 4, WPC = 2; };
 template <> struct Shape<128> { static constexpr int QB = 1, NW = 4, WPC = 2; };
-template <> struct Shape<256> { static constexpr int QB = 1, NW = 4, WPC = 1; };
+template <> struct Shape<256> { static constexpr int QB = 1, NW = 4, WPC = 2; };
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, float c,
