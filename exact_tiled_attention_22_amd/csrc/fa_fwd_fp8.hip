@@ -39,7 +39,10 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
 
 template <int D>
 struct Tile8 {
-    static constexpr int NW = D == 64 ? 4 : 8;
+    // 4-wave workgroups, two per CU (independent workgroups overlap one's matrix work with the
+    // other's softmax better than one 8-wave workgroup does); d = 256 needs 128 KiB: 8 waves, one per CU
+    static constexpr int NW = D == 256 ? 8 : 4;
+    static constexpr int WPC = D == 256 ? 1 : 2;
     static constexpr int THREADS = 64 * NW;
     static constexpr int BN = 64, QW = 32, BM = QW * NW;
     static constexpr int CPR = D / 16;  // 16-byte chunks per row (1-byte elements)
@@ -53,7 +56,7 @@ struct Tile8 {
     static constexpr int OFF_Q = 4 * KV_BYTES;
     static constexpr int LDS_BYTES = 4 * KV_BYTES + Q_BYTES;
     static_assert(LPT >= 1 && CHUNKS % THREADS == 0 && Q_CHUNKS % THREADS == 0, "tiles split evenly");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(LDS_BYTES <= 160 * 1024 / WPC, "LDS budget");
 };
 
 // chunk swizzle of an LDS row (128- or 256-byte rows: 3 bits; 64-byte rows: 2 bits).  Rows read
@@ -289,7 +292,7 @@ struct Fwd8 {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(Tile8<D>::THREADS, 1) void fa_fwd8_kernel(
+__global__ __launch_bounds__(Tile8<D>::THREADS, Tile8<D>::NW * Tile8<D>::WPC / 4) void fa_fwd8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V, __bf16* __restrict__ O,
     float* __restrict__ LSE, const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
     int N, int BH, int ntq, float c, int qflip) {
