@@ -95,6 +95,21 @@ def test_full_size_configs_sampled_rows(cfg_id):
     assert worst_o <= TOL_O and worst_l <= TOL_LSE
 
 
+# long sequences: 64-bit head offsets, thousands of key tiles per query tile, the longest causal skip
+LONG = [("bf16", 64, 262144, True), ("f16", 256, 65536, False), ("bf16", 128, 131072, True)]
+
+
+@pytest.mark.parametrize("dtype,d,N,causal", LONG)
+def test_long_sequence_sampled_rows(dtype, d, N, causal):
+    q, k, v = gen_qkv(1, 1, N, d, dtype, seed=N + d)
+    scale = _f32(1 / math.sqrt(d))
+    o, lse = _run(q, k, v, causal, scale)
+    rng = np.random.default_rng(N)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, N // 2, N - 2, N - 1], rng.integers(0, N, 20)]))
+    o_ref, lse_ref = attention_rows(q[0, 0], k[0, 0], v[0, 0], rows, causal, scale)
+    _compare(o[0, 0][rows], lse[0, 0][rows], o_ref, lse_ref, f"{dtype} d{d} N{N} causal={causal} ({len(rows)} rows)")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_invariants_on_gpu(dtype):
     # constant V -> that constant; causal row 0 -> V[0] exactly (a single weight of 1)
