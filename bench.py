@@ -308,7 +308,7 @@ def main() -> int:
         return ingest_counters(args.config, *args.ingest_counters)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the (b,h) slices would "
-              "shard across GPUs with no communication, but no multi-GPU run is part of this build.",
+              "shard across GPUs with no communication, but this library measures a single GPU.",
               file=sys.stderr)
         return 2
 

@@ -114,7 +114,7 @@ const char* fa_status_str(int status) {
         case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
         case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative or overflowing sizes";
         case FA_ERR_DTYPE: return "FA_ERR_DTYPE: unknown dtype";
-        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: valid request not implemented by this build";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: valid request not implemented by this library";
         case FA_ERR_ALIGN: return "FA_ERR_ALIGN: pointer not 16-byte aligned";
         case FA_ERR_ARG: return "FA_ERR_ARG: invalid argument";
         case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";

@@ -50,7 +50,7 @@ typedef enum {
     FA_ERR_NULL = 1,        /* a required pointer is NULL */
     FA_ERR_SHAPE = 2,       /* negative or overflowing sizes */
     FA_ERR_DTYPE = 3,       /* unknown dtype code */
-    FA_ERR_UNSUPPORTED = 4, /* valid request this build does not implement (e.g. d not in {64,128,256}) */
+    FA_ERR_UNSUPPORTED = 4, /* valid request the library does not implement (e.g. d not in {64,128,256}) */
     FA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
     FA_ERR_ARG = 6,         /* other invalid argument (non-finite scale, causal not 0/1, bad signs) */
     FA_ERR_HIP = 7          /* the HIP runtime rejected a launch */
