@@ -11,7 +11,8 @@ GB/s); --naive times the unfused path (scores, softmax, P*V through HBM) beside 
 Prints ONE JSON line (rank 0):
   metric/value/unit         attention fwd TFLOP/s = 4*B*H*N^2*d (/2 causal) / time per step
   roofline                  dominant kernel: algorithmic flops per launch / average launch time
-                            (HIP events on the launch stream), against the MI355X dense peak
+                            (HIP event pairs around each launch on the launch stream, in a pass
+                            after the timed one), against the MI355X dense peak
   cpu_baseline              the float64 CPU oracle timed on a bounded sample of the same workload
 """
 
@@ -100,6 +101,36 @@ def ingest_counters(cfg_id: int, fetch_csv: str, write_csv: str) -> int:
     return 0
 
 
+def time_steps(step, steps: int, dev) -> float:
+    """Wall-clock ms per step over exactly `steps` back-to-back steps, synchronised on both sides (the
+    launches are enqueued without anything between them, as a caller would issue them)."""
+    import torch
+
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize(dev)
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def launch_ms(step, steps: int, dev) -> float:
+    """Average duration of one step from a HIP event pair recorded around each step on the launch stream
+    (torch's current stream, which the binding launches on); a pass of its own, after the timed one,
+    because the markers between launches keep consecutive kernels from overlapping."""
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
 def cpu_baseline(w, seed: int, budget_s: float = 12.0, bwd: bool = False):
     """Time the float64 oracle on whole heads of the workload until ~budget_s of CPU work."""
     import numpy as np
@@ -169,18 +200,8 @@ def bench_decode(args) -> int:
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize(dev)
-    stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize(dev)
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    avg_ms = sum(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)) / args.steps
+    ms_per_step = time_steps(step, args.steps, dev)
+    avg_ms = launch_ms(step, args.steps, dev)
     nbytes = 2.0 * c["B"] * c["H"] * c["Nk"] * c["d"] * 2
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
@@ -233,25 +254,24 @@ def bench_naive(args, w) -> int:
 
     for _ in range(args.warmup):
         step()
+    # timed region: exactly K back-to-back steps; then each stage from event pairs in a pass of its own
+    ms_per_step = time_steps(step, n, dev)
     torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
     for i in range(n):
         step(ev[i])
     torch.cuda.synchronize(dev)
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / n
     stage_ms = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n)) / n for j in range(3)]
 
     # the fused kernel on the same inputs, same protocol
     o2 = torch.empty_like(q)
     lse2 = torch.empty_like(lse)
+
+    def fused():
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o2, lse=lse2)
+
     for _ in range(args.warmup):
-        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o2, lse=lse2)
-    torch.cuda.synchronize(dev)
-    t1 = time.perf_counter()
-    for _ in range(n):
-        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o2, lse=lse2)
-    torch.cuda.synchronize(dev)
-    fused_ms = (time.perf_counter() - t1) * 1e3 / n
+        fused()
+    fused_ms = time_steps(fused, n, dev)
 
     e = 2
     BH, N, d = w.B * w.H, w.N, w.d
@@ -356,23 +376,9 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize(dev)
-
-    # timed region: K steps, events on the launch stream (torch's current stream) around each step
-    stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    # timed region: exactly K back-to-back steps; then the per-launch duration from event pairs
+    ms_per_step = time_steps(step, args.steps, dev)
+    avg_launch_ms = launch_ms(step, args.steps, dev)
 
     flops = w.flops * (2.5 if args.bwd else 1.0)  # backward: dS, dQ, dK, dV and the recomputed S = 10 N^2 d
     value = flops / (ms_per_step * 1e-3) / 1e12

@@ -3,7 +3,8 @@
 // "Worum es geht" and "Kernpunkte": the classic path writes the large score matrix to HBM and reads it
 // back, several passes instead of about one; glossary "/02 Technische Vorteile im Überblick": the
 // speed-up over it).  It is a measured comparison point, built from three kernels of its own:
-//   1. naive_scores_kernel:  S = scale * Q K^T, float32, [B*H, N, ld]   (MFMA GEMM, 128 x 128 tiles)
+//   1. naive_scores_kernel:  S = scale * Q K^T, float32, [B*H, N, ld]   (MFMA GEMM, 128 x 128 tiles,
+//      computed as S^T blocks so that a lane stores 4 consecutive keys of a row at once)
 //   2. naive_softmax_kernel: P = softmax(S [+ causal mask]) in the input dtype, lse per row (one wave
 //      per row, the row held in registers; rows longer than 8192 are read twice)
 //   3. naive_pv_kernel:      O = P V                               (MFMA GEMM, 128 rows x d per tile)
@@ -97,22 +98,29 @@ struct Scores {
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) acc[i][j] = VT::mfma(a[i], b[j], acc[i][j]);
+                    for (int j = 0; j < 2; ++j) acc[i][j] = VT::mfma(b[j], a[i], acc[i][j]);
             }
         }
-        // accumulator register r of block (i, j) holds S[wm*64 + i*32 + (r/4)*8 + h*4 + r%4][wn*64 + j*32 + n32]
+        // S^T blocks: register r of block (i, j) holds S[query][key] for query wm*64 + i*32 + n32 and
+        // key wn*64 + j*32 + (r/4)*8 + h*4 + r%4, so 4 consecutive registers are 4 consecutive keys of a
+        // row: one 16-byte store each (keys up to ld - 1 exist in every row; N..ld-1 are padding)
         float* Sh = S + (size_t)bh * N * ld;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i) {
+            const int query = m0 + wm * 64 + i * 32 + n32;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int col = n0 + wn * 64 + j * 32 + n32;
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                    if (row < N && col < N) Sh[(size_t)row * ld + col] = acc[i][j][r] * scale;
+                for (int g = 0; g < 4; ++g) {
+                    const int key = n0 + wn * 64 + j * 32 + g * 8 + h * 4;
+                    if (query < N && key < N) {
+                        f32x4 out;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) out[e] = acc[i][j][g * 4 + e] * scale;
+                        *(f32x4*)(Sh + (size_t)query * ld + key) = out;
+                    }
                 }
-            }
+        }
     }
 };
 

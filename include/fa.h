@@ -163,7 +163,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  * the classic path writes the full score matrix to HBM and reads it back; Flash Attention glossary,
  * "/02 Technische Vorteile im Überblick": the speed-up over that path).  Same definition and outputs
  * as fa_fwd, computed in three launches with the N x N matrices in device memory:
- *   fa_naive_scores  : s = scale q k^T, float32 [B*H, N, ld], columns >= N of each row untouched.
+ *   fa_naive_scores  : s = scale q k^T, float32 [B*H, N, ld]; columns >= N of a row are padding
+ *                      (unspecified values).
  *   fa_naive_softmax : p = softmax(s [+ causal mask, key j visible to query i iff j <= i]) per row, of
  *                      type `dtype`, [B*H, N, ld], written as 0 on the masked and padding columns;
  *                      lse [B,H,N] float32 (natural log, may be NULL).  float32 arithmetic, p rounded
