@@ -1,5 +1,5 @@
 """Python binding of libfa.so (ctypes).  Argument marshalling only: every step of the attention
-forward and the fp8 preparation runs in the library's HIP kernels.  torch supplies device memory
+passes (forward, fp8 preparation, backward, decode, unfused path) runs in the library's HIP kernels.  torch supplies device memory
 and the current stream.  There is no fallback: if the library is missing, every call raises.
 """
 
