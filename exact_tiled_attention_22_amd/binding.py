@@ -257,7 +257,7 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = No
         delta=None):
     """Attention backward through fa_bwd: gradients (dq, dk, dv) of fwd's output for the output
     gradient ``dout``; ``o`` and ``lse`` are fwd's results for the same call.  float16/bfloat16, d in
-    {64, 128}.  ``delta`` is the float32 [B, H, N] workspace (allocated when not given)."""
+    {64, 128, 256}.  ``delta`` is the float32 [B, H, N] workspace (allocated when not given)."""
     _check_qkv(q, k, v)
     for t in (o, dout):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:

@@ -173,6 +173,8 @@ struct BwdQ {
                     s[kb] = VT::mfma(*(const x8*)(kl + g.aoff(kb, ks)), qreg[ks], s[kb]);
                     dp[kb] = VT::mfma(*(const x8*)(vl + g.aoff(kb, ks)), dreg[ks], dp[kb]);
                 }
+                if constexpr (D >= 256)
+                    if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
             }
             // dS^T = P^T o (dP^T - D): register r of key block kb holds key kb*32 + (r/8)*16 + h*8 + r%8
             x8 ds[4];
@@ -203,6 +205,9 @@ struct BwdQ {
                     const x4 lo = VT::read_tr(kl + g.toff(cb, st, 0));
                     const x4 hi = VT::read_tr(kl + g.toff(cb, st, 1));
                     acc[cb] = VT::mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), ds[st], acc[cb]);
+                    // d = 256: keep the scheduler from hoisting every operand read of the tile (registers)
+                    if constexpr (D >= 256)
+                        if (cb & 1) __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
@@ -309,6 +314,8 @@ struct BwdKV {
                 const x8 vop = *(const x8*)(smem + (vrow * CPR + ((2 * ks + g.h) ^ bswz<CPR>(vrow))) * 16);
                 s = VT::mfma(*(const x8*)(ql + g.aoff(0, ks)), kreg[ks], s);
                 dp = VT::mfma(*(const x8*)(gl + g.aoff(0, ks)), vop, dp);
+                if constexpr (D >= 256)
+                    if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
             }
             // register r holds query (r/8)*16 + h*8 + r%8 of the tile, key `key`
             x8 pb[2], dsb[2];
@@ -346,6 +353,9 @@ struct BwdKV {
                     const x4 qlo = VT::read_tr(ql + g.toff(cb, st, 0));
                     const x4 qhi = VT::read_tr(ql + g.toff(cb, st, 1));
                     adk[cb] = VT::mfma(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), dsb[st], adk[cb]);
+                    // d = 256: keep the scheduler from hoisting every operand read of the tile (registers)
+                    if constexpr (D >= 256)
+                        if (cb & 1) __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
@@ -374,7 +384,7 @@ struct BwdKV {
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                        const T* __restrict__ V, const T* __restrict__ dO,
                                                        const float* __restrict__ LSE, const float* __restrict__ Dl,
                                                        T* __restrict__ dQ, int N, int BH, int ntq, float c,
@@ -384,7 +394,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(const T* __restrict__ Q, 
 }
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_kv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_kv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                         const T* __restrict__ V, const T* __restrict__ dO,
                                                         const float* __restrict__ LSE, const float* __restrict__ Dl,
                                                         T* __restrict__ dK, T* __restrict__ dV, int N, int BH,
@@ -431,6 +441,9 @@ hipError_t launch_bwd_dt(const void* q, const void* k, const void* v, const void
         case 128:
             return causal ? launch_bwd_t<T, 128, true>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, stream)
                           : launch_bwd_t<T, 128, false>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, stream);
+        case 256:
+            return causal ? launch_bwd_t<T, 256, true>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, stream)
+                          : launch_bwd_t<T, 256, false>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, stream);
         default:
             return hipErrorNotSupported;
     }

@@ -243,7 +243,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
     if (B < 0 || H < 0 || N < 0) return fail(FA_ERR_SHAPE, "negative size B=%d H=%d N=%d", B, H, N);
     if (causal != 0 && causal != 1) return fail(FA_ERR_ARG, "causal must be 0 or 1, got %d", causal);
     if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale must be finite");
-    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "fa_bwd head dimension d=%d (supported: 64, 128)", d);
+    if (d != 64 && d != 128 && d != 256) return fail(FA_ERR_UNSUPPORTED, "fa_bwd head dimension d=%d (supported: 64, 128, 256)", d);
     const long long BH = static_cast<long long>(B) * H;
     if (BH == 0 || N == 0) return FA_OK;
     if (int st = check_sizes(BH, N, d)) return st;

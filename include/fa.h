@@ -148,7 +148,7 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
  *   dq, dk, dv       : DEVICE [B,H,N,d] outputs of type `dtype`; must overlap neither each other nor
  *                      any input.
  *   delta            : DEVICE [B,H,N] float32 workspace owned by the caller; on return it holds D.
- *   d                : 64 or 128 (FA_ERR_UNSUPPORTED otherwise; FA_F32 and FA_FP8_E4M3 likewise).
+ *   d                : 64, 128 or 256 (FA_ERR_UNSUPPORTED otherwise; FA_F32 and FA_FP8_E4M3 likewise).
  * Products accumulate in float32; P and dS are rounded to `dtype` as MFMA operands.  Deterministic:
  * no atomics (dq comes from one pass over the key tiles, dk and dv from one over the query tiles).
  * Returns an fa_status.

@@ -119,7 +119,7 @@ def test_bwd_validation_statuses(lib):
     assert call(dtype=0) == FA_ERR_UNSUPPORTED   # float32 backward is not built
     assert call(dtype=3) == FA_ERR_UNSUPPORTED   # nor fp8
     assert call(dtype=9) == FA_ERR_DTYPE
-    assert call(d=256) == FA_ERR_UNSUPPORTED
+    assert call(d=96) == FA_ERR_UNSUPPORTED
     assert call(causal=3) == FA_ERR_ARG
     assert call(scale=float("nan")) == FA_ERR_ARG
     assert call(N=-2) == FA_ERR_SHAPE

@@ -58,6 +58,7 @@ CASES = [
     ("bf16", 128, 1, False), ("bf16", 128, 17, True), ("bf16", 128, 64, False), ("bf16", 128, 100, True),
     ("bf16", 128, 257, False), ("bf16", 128, 300, True), ("bf16", 64, 130, True), ("bf16", 64, 200, False),
     ("f16", 128, 200, False), ("f16", 128, 333, True), ("f16", 64, 96, True),
+    ("bf16", 256, 100, True), ("f16", 256, 130, False), ("bf16", 256, 65, False), ("f16", 256, 257, True),
 ]
 
 
@@ -92,3 +93,14 @@ def test_bwd_full_size_sampled_heads(causal):
         b, h = divmod(int(bh), H)
         ref = attention_bwd_rows(q[b, h], k[b, h], v[b, h], do[b, h], causal, scale)
         _check([g[b, h] for g in got], ref, f"B16H16N1024 head {b},{h} causal={causal}")
+
+
+def test_bwd_d256_long_sampled_heads():
+    # d = 256 at a longer sequence (fp16 causal, the large-head forward workload's dtype and mask)
+    B, H, N, d = 1, 2, 4096, 256
+    q, k, v, do = _inputs(B, H, N, d, "f16", seed=31)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    got = _gpu_bwd(q, k, v, do, True, scale)
+    for h in range(H):
+        ref = attention_bwd_rows(q[0, h], k[0, h], v[0, h], do[0, h], True, scale)
+        _check([g[0, h] for g in got], ref, f"f16 d256 N{N} head {h} causal=True")
