@@ -31,7 +31,8 @@ struct Decode {
     using VT = Vec<T>;
     using x8 = typename VT::x8;
     using x4 = typename VT::x4;
-    static constexpr int NW = 4, BN = 32, CPR = D / 8, KS = D / 16, CB = D / 32;
+    // waves per workgroup: each wave owns 4 tiles of LDS (64 KiB at d = 256, so two waves there)
+    static constexpr int NW = D >= 256 ? 2 : 4, BN = 32, CPR = D / 8, KS = D / 16, CB = D / 32;
     static constexpr int TILE = BN * CPR * 16;           // one K or V tile
     static constexpr int WAVE_LDS = 4 * TILE;             // K0 | V0 | K1 | V1 per wave
     static constexpr int LDS_BYTES = NW * WAVE_LDS;
@@ -208,7 +209,7 @@ hipError_t launch_decode_t(const void* q, const void* k, const void* v, void* o,
     float* Lp = work + (size_t)BH * nc * Nq * D;
     const long long nwg = (long long)BH * nsplit, nm = (long long)BH * Nq;
     if (nwg > 0x7fffffffLL || nm > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, CAUSAL>), dim3((unsigned)nwg), dim3(256), 0, stream, (const T*)q,
+    hipLaunchKernelGGL((decode_split_kernel<T, D, CAUSAL>), dim3((unsigned)nwg), dim3(64 * Decode<T, D, CAUSAL>::NW), 0, stream, (const T*)q,
                        (const T*)k, (const T*)v, Op, Lp, Nq, Nk, nsplit, chunk, c, qflip);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -228,6 +229,9 @@ hipError_t launch_decode_dt(const void* q, const void* k, const void* v, void* o
         case 128:
             return causal ? launch_decode_t<T, 128, true>(q, k, v, o, lse, work, BH, Nq, Nk, nsplit, chunk, c, qflip, stream)
                           : launch_decode_t<T, 128, false>(q, k, v, o, lse, work, BH, Nq, Nk, nsplit, chunk, c, qflip, stream);
+        case 256:
+            return causal ? launch_decode_t<T, 256, true>(q, k, v, o, lse, work, BH, Nq, Nk, nsplit, chunk, c, qflip, stream)
+                          : launch_decode_t<T, 256, false>(q, k, v, o, lse, work, BH, Nq, Nk, nsplit, chunk, c, qflip, stream);
         default:
             return hipErrorNotSupported;
     }

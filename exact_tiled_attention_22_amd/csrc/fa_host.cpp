@@ -53,14 +53,16 @@ int check_sizes(long long BH, long long N, long long d) {
     return FA_OK;
 }
 
-// Key split of the decode path: enough workgroups (4 waves each) to cover the 256 CUs, chunks of at
-// least 64 keys per wave, chunk length a multiple of the 32-key tile.
-void decode_split(long long BH, long long Nk, int* nsplit, int* chunk) {
+// Key split of the decode path: enough workgroups to cover the 256 CUs, chunks of at least 64 keys per
+// wave, chunk length a multiple of the 32-key tile.  nw = waves per workgroup (4, or 2 at d = 256).
+int decode_waves(int d) { return d >= 256 ? 2 : 4; }
+
+void decode_split(long long BH, long long Nk, int nw, int* nsplit, int* chunk) {
     long long ns = (256 + BH - 1) / BH;
-    const long long maxs = Nk / (4 * 64);
+    const long long maxs = Nk / (nw * 64);
     if (ns > maxs) ns = maxs;
     if (ns < 1) ns = 1;
-    const long long nc = ns * 4;
+    const long long nc = ns * nw;
     long long ck = (Nk + nc - 1) / nc;
     ck = (ck + 31) / 32 * 32;
     *nsplit = static_cast<int>(ns);
@@ -69,8 +71,9 @@ void decode_split(long long BH, long long Nk, int* nsplit, int* chunk) {
 
 size_t decode_bytes(long long BH, int Nq, int Nk, int d) {
     int ns = 1, ck = 32;
-    decode_split(BH, Nk, &ns, &ck);
-    return static_cast<size_t>(BH) * ns * 4 * Nq * (d + 1) * sizeof(float);
+    const int nw = decode_waves(d);
+    decode_split(BH, Nk, nw, &ns, &ck);
+    return static_cast<size_t>(BH) * ns * nw * Nq * (d + 1) * sizeof(float);
 }
 
 // Row stride (elements) of the unfused path's score and probability matrices.
@@ -204,7 +207,8 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return fail(FA_ERR_SHAPE, "negative size B=%d H=%d Nq=%d Nk=%d", B, H, Nq, Nk);
     if (causal != 0 && causal != 1) return fail(FA_ERR_ARG, "causal must be 0 or 1, got %d", causal);
     if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale must be finite");
-    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "fa_fwd_decode head dimension d=%d (supported: 64, 128)", d);
+    if (d != 64 && d != 128 && d != 256)
+        return fail(FA_ERR_UNSUPPORTED, "fa_fwd_decode head dimension d=%d (supported: 64, 128, 256)", d);
     if (Nq > 32) return fail(FA_ERR_UNSUPPORTED, "fa_fwd_decode takes at most 32 queries per head, got %d", Nq);
     if (Nq > Nk) return fail(FA_ERR_SHAPE, "fewer keys (%d) than queries (%d)", Nk, Nq);
     const long long BH = static_cast<long long>(B) * H;
@@ -225,7 +229,7 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
     float c = static_cast<float>(std::fabs(static_cast<double>(scale)) * 1.4426950408889634);
     if (!(c >= 1e-30f)) c = 1e-30f;
     int ns = 1, ck = 32;
-    decode_split(BH, Nk, &ns, &ck);
+    decode_split(BH, Nk, decode_waves(d), &ns, &ck);
     return from_hip(fa::launch_decode_16(dtype == FA_BF16, q, k, v, o, lse, static_cast<float*>(workspace),
                                          static_cast<int>(BH), Nq, Nk, d, causal != 0, ns, ck, c,
                                          std::signbit(scale) ? 0x80008000u : 0u, reinterpret_cast<hipStream_t>(stream)),

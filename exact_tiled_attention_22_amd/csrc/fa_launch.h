@@ -29,13 +29,14 @@ hipError_t launch_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, 
                            const uint64_t sign_bits[4], int block, int BH, int N, int d,
                            hipStream_t stream);
 
-// backward (bf16 / fp16, d in {64, 128}): delta <- rowsum(dout o o), then dq, then dk and dv.
+// backward (bf16 / fp16, d in {64, 128, 256}): delta <- rowsum(dout o o), then dq, then dk and dv.
 hipError_t launch_bwd_16(bool is_bf16, const void* q, const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int N, int d,
                          bool causal, float scale, hipStream_t stream);
 
-// decode (bf16 / fp16, d in {64, 128}, Nq <= 32): split the keys over nsplit workgroups of 4 waves per
-// (b, h), chunks of `chunk` keys per wave; work = float32 [BH, 4 nsplit, Nq, d] then [BH, 4 nsplit, Nq].
+// decode (bf16 / fp16, d in {64, 128, 256}, Nq <= 32): split the keys over nsplit workgroups of NW waves per
+// (b, h) (NW = 4, or 2 at d = 256), chunks of `chunk` keys per wave; work = float32 [BH, NW nsplit, Nq, d]
+// then [BH, NW nsplit, Nq].
 hipError_t launch_decode_16(bool is_bf16, const void* q, const void* k, const void* v, void* o, float* lse, float* work,
                             int BH, int Nq, int Nk, int d, bool causal, int nsplit, int chunk, float c, uint32_t qflip,
                             hipStream_t stream);

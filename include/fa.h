@@ -121,7 +121,7 @@ int fa_fp8_prep(const void* x, int x_dtype, void* x8, float* scales,
  * Nq queries and Nk >= Nq keys per (b, h):
  *   q, o : DEVICE [B,H,Nq,d];  k, v : DEVICE [B,H,Nk,d];  lse : DEVICE [B,H,Nq] float32 or NULL.
  *   causal : 1 = query i sees keys j <= i + Nk - Nq (the queries are the last Nq positions).
- *   dtype : FA_F16 or FA_BF16; d : 64 or 128; 1 <= Nq <= 32 (FA_ERR_UNSUPPORTED otherwise).
+ *   dtype : FA_F16 or FA_BF16; d : 64, 128 or 256; 1 <= Nq <= 32 (FA_ERR_UNSUPPORTED otherwise).
  *   workspace : DEVICE scratch of at least fa_decode_workspace_bytes(B, H, Nq, Nk, d) bytes, owned by
  *               the caller, 16-byte aligned, overlapping no tensor; its contents on return are
  *               unspecified.  Calls that share a workspace must not overlap in time.

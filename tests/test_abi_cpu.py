@@ -155,7 +155,7 @@ def test_decode_validation_statuses(lib):
     # every call below fails validation (or is empty): nothing is launched on these fake pointers
     assert call(dtype=0) == FA_ERR_UNSUPPORTED
     assert call(dtype=7) == FA_ERR_DTYPE
-    assert call(d=256) == FA_ERR_UNSUPPORTED
+    assert call(d=96) == FA_ERR_UNSUPPORTED
     assert call(Nq=33, Nk=1000) == FA_ERR_UNSUPPORTED
     assert call(Nq=5, Nk=4) == FA_ERR_SHAPE
     assert call(causal=2) == FA_ERR_ARG

@@ -51,6 +51,7 @@ CASES = [
     ("bf16", 128, 2, 4, 1, 1000, False), ("bf16", 128, 2, 4, 1, 1000, True), ("bf16", 128, 1, 8, 7, 777, True),
     ("bf16", 64, 2, 2, 32, 2000, True), ("f16", 128, 1, 4, 16, 4096, False), ("bf16", 128, 1, 2, 32, 32, True),
     ("bf16", 128, 3, 5, 5, 100, False), ("f16", 64, 1, 1, 3, 70000, True), ("bf16", 128, 1, 1, 1, 1, False),
+    ("bf16", 256, 2, 4, 1, 1000, True), ("f16", 256, 1, 2, 32, 3000, False), ("bf16", 256, 1, 3, 7, 40000, True),
 ]
 
 
