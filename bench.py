@@ -131,6 +131,52 @@ def launch_ms(step, steps: int, dev) -> float:
     return sum(a.elapsed_time(b) for a, b in ev) / steps
 
 
+def launch_stats(step, steps: int, dev) -> dict:
+    """Mean, median and minimum of the per-step event durations (ms) of a pass of `steps` steps."""
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"avg": sum(t) / len(t), "median": t[len(t) // 2], "min": t[0]}
+
+
+def cold_launch_ms(step, reps: int, dev, flush_bytes: int = 512 << 20) -> float:
+    """Median event-timed duration of a step issued right after a 512 MiB device write, which evicts the
+    inputs from the caches (L2 and the memory-side cache)."""
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+    junk = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
+    t = []
+    for i in range(reps):
+        junk.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize(dev)
+        t.append(a.elapsed_time(b))
+    del junk
+    return sorted(t)[len(t) // 2]
+
+
+def tensor_sha16(t) -> str:
+    """First 16 hex digits of the SHA-256 of a host tensor's bytes (the generated inputs, before upload)."""
+    import torch
+
+    x = t.detach().contiguous().cpu()
+    if x.dtype in (torch.bfloat16, torch.float16):
+        x = x.view(torch.int16)
+    return hashlib.sha256(x.numpy().tobytes()).hexdigest()[:16]
+
+
 def cpu_baseline(w, seed: int, budget_s: float = 12.0, bwd: bool = False):
     """Time the float64 oracle on whole heads of the workload until ~budget_s of CPU work."""
     import numpy as np
@@ -349,8 +395,12 @@ def main() -> int:
         if w.dtype not in ("bf16", "f16"):
             print(f"the backward pass covers bf16/fp16, not workload {w.cfg_id}", file=sys.stderr)
             return 2
-        q, k, v = (t.to(dev) for t in gen_qkv(w.B, w.H, w.N, w.d, w.dtype, seed))
-        do = gen_qkv(w.B, w.H, w.N, w.d, w.dtype, seed + 1000)[0].to(dev)
+        host = gen_qkv(w.B, w.H, w.N, w.d, w.dtype, seed)
+        hashes = {n: tensor_sha16(t) for n, t in zip("qkv", host)}
+        q, k, v = (t.to(dev) for t in host)
+        dh = gen_qkv(w.B, w.H, w.N, w.d, w.dtype, seed + 1000)[0]
+        hashes["dout"] = tensor_sha16(dh)
+        do = dh.to(dev)
         o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
@@ -359,6 +409,7 @@ def main() -> int:
             return fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, delta=delta)
     elif w.dtype == "fp8":
         qs, ks, vs, signs = gen_fp8_workload(w, seed)
+        hashes = {n: tensor_sha16(t) for n, t in zip("qkv", (qs, ks, vs))}
         qs, ks, vs = qs.to(dev), ks.to(dev), vs.to(dev)
 
         def step():
@@ -367,7 +418,10 @@ def main() -> int:
             v8, sv = fa.fp8_prep(vs, None, w.fp8_block)
             return fa.fwd(q8, k8, v8, causal=w.causal, scale=w.scale, fp8_scales=(sq, sk, sv), block=w.fp8_block)
     else:
-        q, k, v = (t.to(dev) for t in gen_qkv(w.B, w.H, w.N, w.d, w.dtype, seed))
+        host = gen_qkv(w.B, w.H, w.N, w.d, w.dtype, seed)
+        hashes = {n: tensor_sha16(t) for n, t in zip("qkv", host)}
+        q, k, v = (t.to(dev) for t in host)
+        del host
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
 
@@ -378,7 +432,9 @@ def main() -> int:
         step()
     # timed region: exactly K back-to-back steps; then the per-launch duration from event pairs
     ms_per_step = time_steps(step, args.steps, dev)
-    avg_launch_ms = launch_ms(step, args.steps, dev)
+    ls = launch_stats(step, args.steps, dev)
+    avg_launch_ms = ls["avg"]
+    cold_ms = cold_launch_ms(step, 20, dev)
 
     flops = w.flops * (2.5 if args.bwd else 1.0)  # backward: dS, dQ, dK, dV and the recomputed S = 10 N^2 d
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -400,7 +456,7 @@ def main() -> int:
         "dtype": {"bf16": "bf16", "f16": "f16", "f32": "f32", "fp8": "fp8_e4m3"}[w.dtype],
         "data": "synthetic (seeded N(0,1), resident in HBM)",
         "config": {"workload": w.name.replace(" fwd", " bwd") if args.bwd else w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "inputs_sha256_16": hashes},
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
@@ -409,6 +465,9 @@ def main() -> int:
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel_avg_ms": round(avg_launch_ms, 5),
+            "kernel_median_ms": round(ls["median"], 5),
+            "kernel_min_ms": round(ls["min"], 5),
+            "cold_kernel_ms": round(cold_ms, 5),
         },
     }
     if args.copy_calibration:
