@@ -260,8 +260,39 @@ def bench_decode(args) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(achieved / 8000.0, 4), "traffic": None, "kernel_avg_ms": round(avg_ms, 5)},
     }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = decode_cpu_baseline(c)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def decode_cpu_baseline(c, budget_s: float = 10.0):
+    """The float64 oracle (attention_rect: full score rows) on whole (b, h) heads of the decode workload
+    until ~budget_s, in the same unit: K/V cache bytes (2 * Nk * d * 2 per head) per second."""
+    import numpy as np  # noqa: F401
+
+    from oracle import attention_rect
+    from synth import gen_qkv
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    qf, k, v = gen_qkv(1, 4, c["Nk"], c["d"], c["dtype"], 7)
+    q = qf[:, :, c["Nk"] - c["Nq"]:, :]
+    scale = 1.0 / math.sqrt(c["d"])
+    heads, t0 = 0, time.perf_counter()
+    while True:
+        h = heads % 4
+        attention_rect(q[0, h], k[0, h], v[0, h], c["causal"], scale)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s or heads >= 4096:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": heads * 2.0 * c["Nk"] * c["d"] * 2 / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} (b,h) heads of the workload (float64 NumPy/OpenBLAS, full score rows), {dt:.1f} s"}
 
 
 def bench_naive(args, w) -> int:
