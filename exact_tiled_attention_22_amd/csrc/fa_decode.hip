@@ -182,6 +182,157 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(const T* __restric
     Decode<T, D, CAUSAL>::run(Q, K, V, Op, Lp, Nq, Nk, nsplit, chunk, c, qflip, smem);
 }
 
+// ---------------------------------------------------------------------------------------------
+// One query per (b, h): S = q K^T and O = P V are dot products, computed on the vector ALU with the
+// packed 16-bit dot instruction (v_dot2_f32_{bf16,f16}, float32 accumulation).  K and V rows stream
+// straight from HBM into registers with ordinary loads, two iterations deep, so the bytes in flight
+// are not bounded by LDS.  Lanes form groups of D/8: lane li of group g holds columns 8 li .. 8 li + 7
+// of key j0 + G t + g (G = 64 / (D/8) keys per load instruction, consecutive rows).  Each group runs
+// an online softmax over its keys; the groups of a wave are combined at the end and the wave writes
+// the same partial (O_c, lse_c) as decode_split_kernel, merged by decode_merge_kernel.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+template <typename T, int D>
+struct DecodeVec {
+    static constexpr int NW = 4, LPK = D / 8, G = 64 / LPK, U = 4;
+    typedef T t2 __attribute__((ext_vector_type(2)));
+
+    static __device__ __forceinline__ float dot2(t2 a, t2 b, float c) {
+        if constexpr (sizeof(T) == 2 && __is_same(T, __bf16)) return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+        else return __builtin_amdgcn_fdot2(a, b, c, false);
+    }
+    // sum over the LPK lanes of a group, result in every lane of the group
+    static __device__ __forceinline__ float group_sum(float x) {
+        x += dppf<0xB1>(x);   // lane ^ 1
+        x += dppf<0x4E>(x);   // lane ^ 2
+        x += dppf<0x141>(x);  // mirror within 8 lanes: the other quad
+        if constexpr (LPK >= 16) x += dppf<0x140>(x);  // mirror within 16 lanes: the other 8
+        if constexpr (LPK >= 32) x += __shfl_xor(x, 16, 64);
+        return x;
+    }
+    static __device__ __forceinline__ void load(const T* __restrict__ Kh, const T* __restrict__ Vh, int j0, int it,
+                                                int g, int last, i32x4 (&kb)[U], i32x4 (&vb)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int key = min(j0 + (it * U + u) * G + g, last);
+            kb[u] = *(const i32x4*)(Kh + (size_t)key * D);
+            vb[u] = *(const i32x4*)(Vh + (size_t)key * D);
+        }
+    }
+
+    static __device__ __forceinline__ void run(const T* __restrict__ Q, const T* __restrict__ K,
+                                               const T* __restrict__ V, float* __restrict__ Op,
+                                               float* __restrict__ Lp, int Nk, int nsplit, int chunk, float c,
+                                               uint32_t qflip) {
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int g = lane / LPK, li = lane % LPK;
+        const int bh = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
+        const int nc = nsplit * NW, ci = split * NW + wave;
+        const int j0 = ci * chunk, j1 = min(Nk, j0 + chunk);
+        const T* Kh = K + (size_t)bh * Nk * D + li * 8;
+        const T* Vh = V + (size_t)bh * Nk * D + li * 8;
+        t2 qv[4];
+        {
+            i32x4 raw = *(const i32x4*)(Q + (size_t)bh * D + li * 8);
+            raw ^= (int)qflip;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                // (a bit-cast applied to a vector element directly would read element 0 each time)
+                const int w = raw[p];
+                qv[p] = __builtin_bit_cast(t2, w);
+            }
+        }
+        float m = -INFINITY, l = 0.0f, o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+        const int niter = j1 > j0 ? (j1 - j0 + G * U - 1) / (G * U) : 0;
+        i32x4 kb[U], vb[U], kn[U], vn[U];
+        if (niter > 0) load(Kh, Vh, j0, 0, g, j1 - 1, kb, vb);
+        for (int it = 0; it < niter; ++it) {
+            if (it + 1 < niter) load(Kh, Vh, j0, it + 1, g, j1 - 1, kn, vn);
+            float sv[U];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int w = kb[u][p];
+                    acc = dot2(qv[p], __builtin_bit_cast(t2, w), acc);
+                }
+                acc = group_sum(acc) * c;
+                const int key = j0 + (it * U + u) * G + g;
+                sv[u] = key < j1 ? acc : -INFINITY;
+                mt = fmaxf(mt, sv[u]);
+            }
+            const float mn = fmaxf(m, mt);
+            // no visible key yet: keep the weights 0 (not exp2 of -inf + inf)
+            const float negm = mn == -INFINITY ? 0.0f : -mn;
+            const float alpha = m == mn ? 1.0f : fast_exp2(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= alpha;
+            m = mn;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float p = fast_exp2(sv[u] + negm);
+                l += p;
+                const T pt = (T)p;  // P rounded to the input type, as the matrix path rounds it
+                const uint32_t pb = (uint32_t)__builtin_bit_cast(uint16_t, pt);
+                const t2 plo = __builtin_bit_cast(t2, pb), phi = __builtin_bit_cast(t2, pb << 16);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int w = vb[u][q];
+                    const t2 vv = __builtin_bit_cast(t2, w);
+                    o[2 * q] = dot2(vv, plo, o[2 * q]);
+                    o[2 * q + 1] = dot2(vv, phi, o[2 * q + 1]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                kb[u] = kn[u];
+                vb[u] = vn[u];
+            }
+        }
+        // combine the groups of the wave: (m, l, o) pairs of groups g and g ^ (off / LPK)
+#pragma unroll
+        for (int off = LPK; off < 64; off *= 2) {
+            const float mo = __shfl_xor(m, off, 64), lo = __shfl_xor(l, off, 64);
+            const float mn = fmaxf(m, mo);
+            const float a = m == mn ? 1.0f : fast_exp2(m - mn), b = mo == mn ? 1.0f : fast_exp2(mo - mn);
+            l = l * a + lo * b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = o[e] * a + __shfl_xor(o[e], off, 64) * b;
+            m = mn;
+        }
+        if (g == 0) {
+            const size_t slot = (size_t)bh * nc + ci;  // Nq = 1
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+            f32x4 a, b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] = o[e] * inv;
+                b[e] = o[4 + e] * inv;
+            }
+            *(f32x4*)(Op + slot * D + li * 8) = a;
+            *(f32x4*)(Op + slot * D + li * 8 + 4) = b;
+            if (li == 0) Lp[slot] = l > 0.0f ? m + __log2f(l) : -INFINITY;
+        }
+    }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_vec_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                         const T* __restrict__ V, float* __restrict__ Op,
+                                                         float* __restrict__ Lp, int Nk, int nsplit, int chunk, float c,
+                                                         uint32_t qflip) {
+    DecodeVec<T, D>::run(Q, K, V, Op, Lp, Nk, nsplit, chunk, c, qflip);
+}
+
 // one workgroup of D threads per (b, h, query): thread t owns output column t
 template <typename T, int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ Op, const float* __restrict__ Lp,
@@ -204,13 +355,20 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_decode_t(const void* q, const void* k, const void* v, void* o, float* lse, float* work, int BH,
                            int Nq, int Nk, int nsplit, int chunk, float c, uint32_t qflip, hipStream_t stream) {
-    const int nc = nsplit * Decode<T, D, CAUSAL>::NW;
+    // one query: the vector-ALU kernel (its causal mask hides nothing: the query is the last position)
+    const bool vec = Nq == 1;
+    const int nc = nsplit * (vec ? DecodeVec<T, D>::NW : Decode<T, D, CAUSAL>::NW);
     float* Op = work;
     float* Lp = work + (size_t)BH * nc * Nq * D;
     const long long nwg = (long long)BH * nsplit, nm = (long long)BH * Nq;
     if (nwg > 0x7fffffffLL || nm > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, CAUSAL>), dim3((unsigned)nwg), dim3(64 * Decode<T, D, CAUSAL>::NW), 0, stream, (const T*)q,
-                       (const T*)k, (const T*)v, Op, Lp, Nq, Nk, nsplit, chunk, c, qflip);
+    if (vec) {
+        hipLaunchKernelGGL((decode_vec_kernel<T, D>), dim3((unsigned)nwg), dim3(64 * DecodeVec<T, D>::NW), 0, stream,
+                           (const T*)q, (const T*)k, (const T*)v, Op, Lp, Nk, nsplit, chunk, c, qflip);
+    } else {
+        hipLaunchKernelGGL((decode_split_kernel<T, D, CAUSAL>), dim3((unsigned)nwg), dim3(64 * Decode<T, D, CAUSAL>::NW), 0, stream, (const T*)q,
+                           (const T*)k, (const T*)v, Op, Lp, Nq, Nk, nsplit, chunk, c, qflip);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)nm), dim3(D), 0, stream, (const float*)Op,

@@ -53,26 +53,28 @@ int check_sizes(long long BH, long long N, long long d) {
     return FA_OK;
 }
 
-// Key split of the decode path: enough workgroups to cover the 256 CUs, chunks of at least 64 keys per
-// wave, chunk length a multiple of the 32-key tile.  nw = waves per workgroup (4, or 2 at d = 256).
-int decode_waves(int d) { return d >= 256 ? 2 : 4; }
-
-void decode_split(long long BH, long long Nk, int nw, int* nsplit, int* chunk) {
-    long long ns = (256 + BH - 1) / BH;
-    const long long maxs = Nk / (nw * 64);
+// Key split of the decode path.  One query (the vector-ALU kernel, 4 waves per workgroup, no LDS):
+// about 16 waves per CU, chunks of at least 256 keys.  Several queries (the matrix kernel, 4 waves per
+// workgroup or 2 at d = 256, one workgroup per CU by LDS): enough workgroups to cover the 256 CUs,
+// chunks of at least 64 keys per wave.  Chunk lengths are multiples of 32 keys.
+void decode_plan(long long BH, int Nq, long long Nk, int d, int* nw, int* nsplit, int* chunk) {
+    const bool vec = Nq == 1;
+    const int w = vec ? 4 : (d >= 256 ? 2 : 4);
+    long long ns = vec ? (1024 + BH - 1) / BH : (256 + BH - 1) / BH;
+    const long long maxs = Nk / (w * (vec ? 256 : 64));
     if (ns > maxs) ns = maxs;
     if (ns < 1) ns = 1;
-    const long long nc = ns * nw;
+    const long long nc = ns * w;
     long long ck = (Nk + nc - 1) / nc;
     ck = (ck + 31) / 32 * 32;
+    *nw = w;
     *nsplit = static_cast<int>(ns);
     *chunk = static_cast<int>(ck);
 }
 
 size_t decode_bytes(long long BH, int Nq, int Nk, int d) {
-    int ns = 1, ck = 32;
-    const int nw = decode_waves(d);
-    decode_split(BH, Nk, nw, &ns, &ck);
+    int nw = 4, ns = 1, ck = 32;
+    decode_plan(BH, Nq, Nk, d, &nw, &ns, &ck);
     return static_cast<size_t>(BH) * ns * nw * Nq * (d + 1) * sizeof(float);
 }
 
@@ -228,8 +230,8 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
     if (lse && overlaps(lse, static_cast<size_t>(BH) * Nq * 4, o, qb)) return fail(FA_ERR_ARG, "lse must not overlap o");
     float c = static_cast<float>(std::fabs(static_cast<double>(scale)) * 1.4426950408889634);
     if (!(c >= 1e-30f)) c = 1e-30f;
-    int ns = 1, ck = 32;
-    decode_split(BH, Nk, decode_waves(d), &ns, &ck);
+    int nw = 4, ns = 1, ck = 32;
+    decode_plan(BH, Nq, Nk, d, &nw, &ns, &ck);
     return from_hip(fa::launch_decode_16(dtype == FA_BF16, q, k, v, o, lse, static_cast<float*>(workspace),
                                          static_cast<int>(BH), Nq, Nk, d, causal != 0, ns, ck, c,
                                          std::signbit(scale) ? 0x80008000u : 0u, reinterpret_cast<hipStream_t>(stream)),

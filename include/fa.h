@@ -127,6 +127,7 @@ int fa_fp8_prep(const void* x, int x_dtype, void* x8, float* scales,
  *               unspecified.  Calls that share a workspace must not overlap in time.
  * The keys are split into chunks handled by independent waves (per-chunk online softmax), and a
  * second launch merges the chunks' (O, lse) pairs; float32 accumulation, P rounded to `dtype`.
+ * Nq = 1 runs its dot products on the vector ALU, Nq > 1 on the matrix cores.
  * Returns an fa_status.
  */
 size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
