@@ -52,6 +52,9 @@ CASES = [
     ("bf16", 64, 2, 2, 32, 2000, True), ("f16", 128, 1, 4, 16, 4096, False), ("bf16", 128, 1, 2, 32, 32, True),
     ("bf16", 128, 3, 5, 5, 100, False), ("f16", 64, 1, 1, 3, 70000, True), ("bf16", 128, 1, 1, 1, 1, False),
     ("bf16", 256, 2, 4, 1, 1000, True), ("f16", 256, 1, 2, 32, 3000, False), ("bf16", 256, 1, 3, 7, 40000, True),
+    # one query (the vector-ALU kernel): every head dimension and both types, ragged chunk ends
+    ("f16", 64, 2, 3, 1, 5003, False), ("bf16", 64, 1, 2, 1, 77, True), ("f16", 128, 3, 3, 1, 20001, False),
+    ("f16", 256, 1, 5, 1, 9999, True),
 ]
 
 
