@@ -76,6 +76,15 @@ def test_decode_matches_forward_when_square_and_negative_scale():
     assert float(np.abs(of.float().cpu().numpy() - o).max()) <= 1e-2
 
 
+@pytest.mark.parametrize("scale", [-0.0883883476, 0.0, 1.5])
+def test_decode_single_query_scales(scale):
+    # one query: negative scale (q sign-flipped), zero scale (uniform weights) and a large scale
+    q, k, v = _inputs(2, 2, 1, 3000, 128, "bf16", seed=6)
+    s = float(np.float32(scale))
+    o, lse = _run(q, k, v, False, s)
+    _check(o, lse, q, k, v, False, s, f"Nq1 scale={s}")
+
+
 def test_decode_large_cache_sampled_heads():
     # B8 H32, one query against a 32768-key cache (the bench's decode workload); four heads checked
     q, k, v = _inputs(8, 32, 1, 32768, 128, "bf16", seed=8)
