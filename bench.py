@@ -230,7 +230,10 @@ def bench_decode(args) -> int:
     import exact_tiled_attention_22_amd as fa
     from synth import gen_qkv
 
-    c = DECODE
+    c = dict(DECODE, Nq=args.nq)
+    if not 1 <= c["Nq"] <= 32:
+        print(f"--nq must be 1..32 (the decode path takes at most 32 queries), got {c['Nq']}", file=sys.stderr)
+        return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     qf, k, v = (t.to(dev) for t in gen_qkv(c["B"], c["H"], c["Nk"], c["d"], c["dtype"], 7))
@@ -256,7 +259,7 @@ def bench_decode(args) -> int:
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,1), resident in HBM)",
-        "config": {"workload": "bf16 decode B8 H32 Nq1 Nk32768 d128 non-causal", **c, "parallelism": "single GPU"},
+        "config": {"workload": f"bf16 decode B8 H32 Nq{c['Nq']} Nk32768 d128 non-causal", **c, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(achieved / 8000.0, 4), "traffic": None, "kernel_avg_ms": round(avg_ms, 5)},
     }
@@ -391,6 +394,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", action="store_true",
                     help="time the decode path (1 query against a 32768-key cache, B8 H32 d128 bf16)")
+    ap.add_argument("--nq", type=int, default=1,
+                    help="queries per (b, h) for --decode (1: vector-ALU kernel; 2..32: matrix kernel)")
     ap.add_argument("--naive", action="store_true",
                     help="time the unfused path (S and P through HBM) and the fused kernel beside it")
     ap.add_argument("--bwd", action="store_true",
