@@ -13,8 +13,9 @@ What it computes, in float64 on the CPU, straight from the definitions:
   Flash Attention glossary, "/01 Was ist Flash Attention?").
 * ``attention_probs`` — the score and probability matrices of one head, as the unfused comparison path
   holds them in memory.
-* ``attention_rect`` — the same definition for Nq queries against Nk >= Nq cached keys (the decode
-  shape), with the causal mask aligned to the end of the key sequence.
+* ``attention_rect`` — the same definition for Nq queries against Nk keys, the queries sitting at
+  positions q_start .. q_start + Nq - 1 of the key sequence for the causal mask (default: the last Nq
+  positions, the decode shape; a middle range is one GPU's share of a sequence-sharded forward).
 * ``attention_bwd_ref`` / ``attention_bwd_rows`` — the gradients dQ, dK, dV of that definition for a
   given output gradient dO (the pages name the backward pass but do not write it out; the derivative
   of the definition is the plain result the kernels must reproduce).

@@ -116,18 +116,22 @@ def attention_bwd_ref(q, k, v, do, causal: bool, scale: float):
     return dq, dk, dv
 
 
-def attention_rect(qh, kh, vh, causal: bool, scale: float):
-    """Attention of Nq queries against Nk >= Nq keys for ONE head (the decode shape: the queries are the
-    last Nq positions of a sequence whose keys are all cached).  Causal means query i sees keys
-    j <= i + (Nk - Nq) (the mask aligned to the end of the key sequence); with Nq == Nk this is the
-    lower-triangular mask of attention_rows.  Returns (O [Nq, d], lse [Nq]) in float64, full score
-    rows, same definition as attention_rows.
+def attention_rect(qh, kh, vh, causal: bool, scale: float, q_start=None):
+    """Attention of Nq queries against Nk keys for ONE head, same definition as attention_rows with full
+    score rows.  The queries are the positions q_start .. q_start + Nq - 1 of the key sequence: causal
+    means query i sees keys j <= q_start + i.  q_start defaults to Nk - Nq (the queries are the last Nq
+    positions, the decode shape, mask aligned to the end of the key sequence); with Nq == Nk and
+    q_start = 0 this is the lower-triangular mask of attention_rows.  Rows of a query range taken from
+    the middle of a sequence (q_start + Nq < Nk) see a prefix of the keys only.  q_start is ignored
+    when causal is false.  Returns (O [Nq, d], lse [Nq]) in float64.
     """
     qh, kh, vh = _f64(qh), _f64(kh), _f64(vh)
     nq, nk = qh.shape[0], kh.shape[0]
     s = float(scale) * (qh @ kh.T)
     if causal:
-        s = np.where(np.arange(nk)[None, :] <= np.arange(nq)[:, None] + (nk - nq), s, -np.inf)
+        start = nk - nq if q_start is None else int(q_start)
+        assert start >= 0, "causal queries start at a key position >= 0"
+        s = np.where(np.arange(nk)[None, :] <= np.arange(nq)[:, None] + start, s, -np.inf)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
     l = e.sum(axis=1, keepdims=True)
