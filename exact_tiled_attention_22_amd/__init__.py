@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     fwd,
     fwd_decode,
     fwd_naive,
+    fwd_rect,
     last_error,
     lib,
     naive_pv,

@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_ex.restype = i
     L.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
     L.fa_bwd.restype = i
+    L.fa_fwd_rect.argtypes = [vp] * 5 + [i] * 7 + [f, i, vp]
+    L.fa_fwd_rect.restype = i
     L.fa_fwd_decode.argtypes = [vp] * 5 + [i] * 6 + [f, i, vp, ctypes.c_size_t, vp]
     L.fa_fwd_decode.restype = i
     L.fa_decode_workspace_bytes.argtypes = [i] * 5
@@ -111,6 +113,26 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _out(t, shape, dtype, device, name):
+    """A caller-supplied output must have exactly the size the kernels write (the C ABI takes bare
+    pointers and cannot check it); None allocates one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    return t
+
+
+def _workspace(ws, need, device):
+    """A uint8 device workspace of at least ``need`` bytes (allocated when None)."""
+    if ws is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if ws.dtype != torch.uint8 or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
+    return ws  # the library checks the size against the bytes it needs
+
+
 def _check_qkv(q, k, v):
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
@@ -136,10 +158,9 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
         scale = 1.0 / math.sqrt(d)
     code = DTYPE_CODE[q.dtype]
     out_dtype = torch.bfloat16 if code == FA_FP8_E4M3 else q.dtype
-    if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    if return_lse and lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    out = _out(out, q.shape, out_dtype, q.device, "out")
+    if return_lse:
+        lse = _out(lse, (B, H, N), torch.float32, q.device, "lse")
     s8 = None
     keep = []
     if code == FA_FP8_E4M3 and fp8_scales is not None:
@@ -151,6 +172,30 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
     del keep
     _check(st, "fa_fwd_ex")
     return out, (lse if return_lse else None)
+
+
+def fwd_rect(q, k, v, *, causal: bool = False, q_start: int | None = None, scale: float | None = None, out=None,
+             lse=None):
+    """Attention of q [B, H, Nq, d] against k, v [B, H, Nk, d] through fa_fwd_rect.  Causal: query i
+    sits at position q_start + i of the key sequence (default Nk - Nq, the last Nq positions); non-causal
+    takes q_start 0.  Returns (o, lse)."""
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v must be contiguous 4-D GPU tensors")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must be [B, H, Nk, d] of q's dtype")
+    if q_start is None:
+        q_start = Nk - Nq if causal else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = _out(out, q.shape, q.dtype, q.device, "out")
+    lse = _out(lse, (B, H, Nq), torch.float32, q.device, "lse")
+    st = lib().fa_fwd_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, int(q_start), d,
+                           int(bool(causal)), float(scale), DTYPE_CODE[q.dtype], _stream(q.device))
+    _check(st, "fa_fwd_rect")
+    return out, lse
 
 
 def decode_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
@@ -170,11 +215,10 @@ def fwd_decode(q, k, v, *, causal: bool = False, scale: float | None = None, out
         raise ValueError("k and v must be [B, H, Nk, d] of q's dtype")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    out = _out(out, q.shape, q.dtype, q.device, "out")
+    lse = _out(lse, (B, H, Nq), torch.float32, q.device, "lse")
     need = decode_workspace_bytes(B, H, Nq, Nk, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     st = lib().fa_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, int(bool(causal)),
                              float(scale), DTYPE_CODE[q.dtype], _ptr(workspace), workspace.numel(), _stream(q.device))
     _check(st, "fa_fwd_decode")
@@ -196,8 +240,7 @@ def naive_scores(q, k, *, scale: float | None = None, s=None):
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if s is None:
-        s = torch.empty((B, H, N, naive_row_stride(N)), dtype=torch.float32, device=q.device)
+    s = _out(s, (B, H, N, naive_row_stride(N)), torch.float32, q.device, "s")
     st = lib().fa_naive_scores(_ptr(q), _ptr(k), _ptr(s), B, H, N, d, float(scale), DTYPE_CODE[q.dtype],
                                _stream(q.device))
     _check(st, "fa_naive_scores")
@@ -212,10 +255,8 @@ def naive_softmax(s, *, dtype, causal: bool = False, p=None, lse=None):
     B, H, N, ld = s.shape
     if ld != naive_row_stride(N):
         raise ValueError(f"s rows must be {naive_row_stride(N)} elements apart, got {ld}")
-    if p is None:
-        p = torch.empty(s.shape, dtype=dtype, device=s.device)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=s.device)
+    p = _out(p, s.shape, dtype, s.device, "p")
+    lse = _out(lse, (B, H, N), torch.float32, s.device, "lse")
     st = lib().fa_naive_softmax(_ptr(s), _ptr(p), _ptr(lse), B, H, N, int(bool(causal)), DTYPE_CODE[dtype],
                                 _stream(s.device))
     _check(st, "fa_naive_softmax")
@@ -229,8 +270,7 @@ def naive_pv(p, v, *, out=None):
     B, H, N, d = v.shape
     if p.shape != (B, H, N, naive_row_stride(N)) or p.dtype != v.dtype:
         raise ValueError("p must be [B, H, N, ld] of v's dtype")
-    if out is None:
-        out = torch.empty_like(v)
+    out = _out(out, v.shape, v.dtype, v.device, "out")
     st = lib().fa_naive_pv(_ptr(p), _ptr(v), _ptr(out), B, H, N, d, DTYPE_CODE[v.dtype], _stream(v.device))
     _check(st, "fa_naive_pv")
     return out
@@ -243,10 +283,9 @@ def fwd_naive(q, k, v, *, causal: bool = False, scale: float | None = None, out=
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    if workspace is None:
-        workspace = torch.empty(max(naive_workspace_bytes(B, H, N), 16), dtype=torch.uint8, device=q.device)
+    out = _out(out, q.shape, q.dtype, q.device, "out")
+    lse = _out(lse, (B, H, N), torch.float32, q.device, "lse")
+    workspace = _workspace(workspace, naive_workspace_bytes(B, H, N), q.device)
     st = lib().fa_fwd_naive(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, int(bool(causal)),
                             float(scale), DTYPE_CODE[q.dtype], _ptr(workspace), workspace.numel(), _stream(q.device))
     _check(st, "fa_fwd_naive")
@@ -267,10 +306,10 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = No
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    dq = _out(dq, q.shape, q.dtype, q.device, "dq")
+    dk = _out(dk, q.shape, q.dtype, q.device, "dk")
+    dv = _out(dv, q.shape, q.dtype, q.device, "dv")
+    delta = _out(delta, (B, H, N), torch.float32, q.device, "delta")
     st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                       _ptr(delta), B, H, N, d, int(bool(causal)), float(scale), DTYPE_CODE[q.dtype],
                       _stream(q.device))
@@ -291,10 +330,8 @@ def fp8_prep(x, signs=None, block: int = 64, out=None, scales=None):
     N, d = x.shape[-2], x.shape[-1]
     BH = x.numel() // max(1, N * d) if N * d else int(math.prod(x.shape[:-2]))
     nblk = -(-N // block) if block > 0 else 0
-    if out is None:
-        out = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
-    if scales is None:
-        scales = torch.empty(tuple(x.shape[:-2]) + (max(nblk, 0),), dtype=torch.float32, device=x.device)
+    out = _out(out, x.shape, torch.float8_e4m3fn, x.device, "out")
+    scales = _out(scales, tuple(x.shape[:-2]) + (max(nblk, 0),), torch.float32, x.device, "scales")
     sign_buf = None
     if signs is not None:
         sign_list = [int(s) for s in (signs.tolist() if hasattr(signs, "tolist") else signs)]

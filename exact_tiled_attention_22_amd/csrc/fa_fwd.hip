@@ -130,18 +130,19 @@ struct Fwd {
         }
     }
 
-    // Hide keys past N and (causal) keys after the query; true when the tile needs it.
-    static __device__ __forceinline__ void mask(f32x16 (&s)[QB][NKB], int kv0, int N, int q0w, int n32, int h) {
-        if ((kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > q0w)) {
+    // Hide keys past Nk and (causal) keys after the query's position; qp0 is the position in the key
+    // sequence of the wave's first query row.  Only tiles that need it pay for the compares.
+    static __device__ __forceinline__ void mask(f32x16 (&s)[QB][NKB], int kv0, int Nk, int qp0, int n32, int h) {
+        if ((kv0 + BN > Nk) || (CAUSAL && kv0 + BN - 1 > qp0)) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                const int query = q0w + qb * 32 + n32;
+                const int query = qp0 + qb * 32 + n32;
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kv0 + kb * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
-                        if (key >= N || (CAUSAL && key > query)) s[qb][kb][r] = -INFINITY;
+                        if (key >= Nk || (CAUSAL && key > query)) s[qb][kb][r] = -INFINITY;
                     }
             }
         }
@@ -258,14 +259,14 @@ struct Fwd {
     // O = acc / l rounded to T (lane holds 16 columns of its query per 32-column block), and
     // lse = ln2 * (m + log2 l)
     static __device__ __forceinline__ void epilogue(T* __restrict__ O, float* __restrict__ LSE, size_t head, int bh,
-                                                    int N, int q0w, int n32, int h, const f32x16 (&oacc)[QB][CB],
+                                                    int Nq, int q0w, int n32, int h, const f32x16 (&oacc)[QB][CB],
                                                     const float (&m_run)[QB], const float (&l_run)[QB]) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const float lt = halves_sum(l_run[qb]);
             const float inv = 1.0f / lt;
             const int query = q0w + qb * 32 + n32;
-            if (query < N) {
+            if (query < Nq) {
                 T* orow = O + head + (size_t)query * D;
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
@@ -277,7 +278,7 @@ struct Fwd {
                         *(x4*)(orow + cb * 32 + g * 8 + h * 4) = out;
                     }
                 if (LSE != nullptr && h == 0)
-                    LSE[(size_t)bh * N + query] = (m_run[qb] + __log2f(lt)) * 0.69314718055994531f;
+                    LSE[(size_t)bh * Nq + query] = (m_run[qb] + __log2f(lt)) * 0.69314718055994531f;
             }
         }
     }
@@ -287,8 +288,8 @@ struct Fwd {
     // then its softmax, whose exponentials interleave with the value MFMAs.
     static __device__ __forceinline__ void run_seq(const T* __restrict__ Q, const T* __restrict__ K,
                                                    const T* __restrict__ V, T* __restrict__ O,
-                                                   float* __restrict__ LSE, int N, int BH, int ntq, float c,
-                                                   uint32_t qflip, char* smem) {
+                                                   float* __restrict__ LSE, int Nq, int Nk, int qpos, int BH,
+                                                   int ntq, float c, uint32_t qflip, char* smem) {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -297,14 +298,15 @@ struct Fwd {
         const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
         int bh, qt;
         map_block(blockIdx.x, BH, ntq, CAUSAL, bh, qt);
-        const size_t head = (size_t)bh * N * D;
+        const size_t head = (size_t)bh * Nq * D;  // Q, O
+        const size_t headk = (size_t)bh * Nk * D; // K, V
         const T* Qh = Q + head;
-        const T* Kh = K + head;
-        const T* Vh = V + head;
+        const T* Kh = K + headk;
+        const T* Vh = V + headk;
         const int q0 = qt * BM;
         const int q0w = q0 + wave * QW;
-        const int nt = ((CAUSAL ? min(N, q0 + BM) : N) + BN - 1) / BN;
-        const int ntw = ((CAUSAL ? min(N, q0w + QW) : N) + BN - 1) / BN;
+        const int nt = ((CAUSAL ? min(Nk, qpos + q0 + BM) : Nk) + BN - 1) / BN;
+        const int ntw = ((CAUSAL ? min(Nk, qpos + q0w + QW) : Nk) + BN - 1) / BN;
         Lane ln;
         ln.kperm = ((n32 >> 4) & 1) * 16 + ((n32 >> 2) & 1) * 8 + ((n32 >> 3) & 1) * 4 + (n32 & 3);
         ln.h = h;
@@ -318,7 +320,7 @@ struct Fwd {
         x8 qreg[QB][KS];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const T* src = Qh + (size_t)min(q0w + qb * 32 + n32, N - 1) * D + h * 8;
+            const T* src = Qh + (size_t)min(q0w + qb * 32 + n32, Nq - 1) * D + h * 8;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 i32x4 raw = *(const i32x4*)(src + ks * 16);
@@ -326,8 +328,8 @@ struct Fwd {
                 qreg[qb][ks] = __builtin_bit_cast(x8, raw);
             }
         }
-        copy_rows<LPT>(Kh, 0, N, lbase + OFF_K0, tid, wave);
-        copy_rows<LPT>(Vh, 0, N, lbase + OFF_V0, tid, wave);
+        copy_rows<LPT>(Kh, 0, Nk, lbase + OFF_K0, tid, wave);
+        copy_rows<LPT>(Vh, 0, Nk, lbase + OFF_V0, tid, wave);
         f32x16 oacc[QB][CB];
         float m_run[QB], l_run[QB];
 #pragma unroll
@@ -341,13 +343,13 @@ struct Fwd {
             wait_vmcnt<0>();
             lds_barrier();  // K_j, V_j visible; the other stage is free
             if (j + 1 < nt) {
-                copy_rows<LPT>(Kh, (j + 1) * BN, N, lbase + dk, tid, wave);
-                copy_rows<LPT>(Vh, (j + 1) * BN, N, lbase + dv, tid, wave);
+                copy_rows<LPT>(Kh, (j + 1) * BN, Nk, lbase + dk, tid, wave);
+                copy_rows<LPT>(Vh, (j + 1) * BN, Nk, lbase + dv, tid, wave);
             }
             if (j < ntw) {
                 f32x16 sc[QB][NKB];
                 scores(smem + ok, qreg, sc, ln);
-                mask(sc, j * BN, N, q0w, n32, h);
+                mask(sc, j * BN, Nk, qpos + q0w, n32, h);
                 update_max(sc, c, oacc, m_run, l_run);
                 x8 p[QB][2 * NKB];
                 exps(sc, c, m_run, l_run, p);
@@ -358,13 +360,13 @@ struct Fwd {
             iteration(j, OFF_K0, OFF_V0, OFF_K1, OFF_V1);
             if (j + 1 < nt) iteration(j + 1, OFF_K1, OFF_V1, OFF_K0, OFF_V0);
         }
-        epilogue(O, LSE, head, bh, N, q0w, n32, h, oacc, m_run, l_run);
+        epilogue(O, LSE, head, bh, Nq, q0w, n32, h, oacc, m_run, l_run);
     }
 
     static __device__ __forceinline__ void run(const T* __restrict__ Q, const T* __restrict__ K,
                                                const T* __restrict__ V, T* __restrict__ O,
-                                               float* __restrict__ LSE, int N, int BH, int ntq, float c,
-                                               uint32_t qflip, char* smem) {
+                                               float* __restrict__ LSE, int Nq, int Nk, int qpos, int BH,
+                                               int ntq, float c, uint32_t qflip, char* smem) {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -374,14 +376,15 @@ struct Fwd {
 
         int bh, qt;
         map_block(blockIdx.x, BH, ntq, CAUSAL, bh, qt);
-        const size_t head = (size_t)bh * N * D;
+        const size_t head = (size_t)bh * Nq * D;  // Q, O
+        const size_t headk = (size_t)bh * Nk * D; // K, V
         const T* Qh = Q + head;
-        const T* Kh = K + head;
-        const T* Vh = V + head;
+        const T* Kh = K + headk;
+        const T* Vh = V + headk;
         const int q0 = qt * BM;
         const int q0w = q0 + wave * QW;
-        const int nt = ((CAUSAL ? min(N, q0 + BM) : N) + BN - 1) / BN;   // tiles of the workgroup
-        const int ntw = ((CAUSAL ? min(N, q0w + QW) : N) + BN - 1) / BN; // tiles this wave computes
+        const int nt = ((CAUSAL ? min(Nk, qpos + q0 + BM) : Nk) + BN - 1) / BN;   // tiles of the workgroup
+        const int ntw = ((CAUSAL ? min(Nk, qpos + q0w + QW) : Nk) + BN - 1) / BN; // tiles this wave computes
 
         Lane ln;
         ln.kperm = ((n32 >> 4) & 1) * 16 + ((n32 >> 2) & 1) * 8 + ((n32 >> 3) & 1) * 4 + (n32 & 3);
@@ -398,7 +401,7 @@ struct Fwd {
         x8 qreg[QB][KS];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const T* src = Qh + (size_t)min(q0w + qb * 32 + n32, N - 1) * D + h * 8;
+            const T* src = Qh + (size_t)min(q0w + qb * 32 + n32, Nq - 1) * D + h * 8;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 i32x4 raw = *(const i32x4*)(src + ks * 16);
@@ -406,9 +409,9 @@ struct Fwd {
                 qreg[qb][ks] = __builtin_bit_cast(x8, raw);
             }
         }
-        copy_rows<LPT>(Kh, 0, N, lbase + OFF_K0, tid, wave);
-        copy_rows<LPT>(Vh, 0, N, lbase + OFF_V0, tid, wave);
-        if (nt > 1) copy_rows<LPT>(Kh, BN, N, lbase + OFF_K1, tid, wave);
+        copy_rows<LPT>(Kh, 0, Nk, lbase + OFF_K0, tid, wave);
+        copy_rows<LPT>(Vh, 0, Nk, lbase + OFF_V0, tid, wave);
+        if (nt > 1) copy_rows<LPT>(Kh, BN, Nk, lbase + OFF_K1, tid, wave);
         wait_vmcnt<0>();
         lds_barrier();
 
@@ -430,10 +433,10 @@ struct Fwd {
                              uint32_t dv) {
             wait_vmcnt<0>();
             lds_barrier();
-            if (j + 2 < nt) copy_rows<LPT>(Kh, (j + 2) * BN, N, lbase + dk, tid, wave);
-            if (j + 1 < nt) copy_rows<LPT>(Vh, (j + 1) * BN, N, lbase + dv, tid, wave);
+            if (j + 2 < nt) copy_rows<LPT>(Kh, (j + 2) * BN, Nk, lbase + dk, tid, wave);
+            if (j + 1 < nt) copy_rows<LPT>(Vh, (j + 1) * BN, Nk, lbase + dv, tid, wave);
             if (j < ntw) {
-                mask(cur, j * BN, N, q0w, n32, h);
+                mask(cur, j * BN, Nk, qpos + q0w, n32, h);
                 update_max(cur, c, oacc, m_run, l_run);
                 // next tile's scores (its K stage always holds valid data; on the last tile the result is
                 // unused) in the same basic block as this tile's exponentials so the two overlap; with
@@ -456,7 +459,7 @@ struct Fwd {
             if (j + 1 < nt) iteration(j + 1, s1, s0, OFF_K0, OFF_V1, OFF_K1, OFF_V0);
         }
 
-        epilogue(O, LSE, head, bh, N, q0w, n32, h, oacc, m_run, l_run);
+        epilogue(O, LSE, head, bh, Nq, q0w, n32, h, oacc, m_run, l_run);
     }
 };
 
@@ -465,12 +468,12 @@ struct Fwd {
 template <typename T, int D, int QB, int NW, int WPC, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW, (NW * WPC) / 4) void fa_fwd16_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
-    float* __restrict__ LSE, int N, int BH, int ntq, float c, uint32_t qflip) {
+    float* __restrict__ LSE, int Nq, int Nk, int qpos, int BH, int ntq, float c, uint32_t qflip) {
     __shared__ __attribute__((aligned(1024))) char smem[Tile<D, QB, NW, WPC>::LDS_BYTES];
     if constexpr (D <= 128)
-        Fwd<T, D, QB, NW, WPC, CAUSAL>::run(Q, K, V, O, LSE, N, BH, ntq, c, qflip, smem);
+        Fwd<T, D, QB, NW, WPC, CAUSAL>::run(Q, K, V, O, LSE, Nq, Nk, qpos, BH, ntq, c, qflip, smem);
     else
-        Fwd<T, D, QB, NW, WPC, CAUSAL>::run_seq(Q, K, V, O, LSE, N, BH, ntq, c, qflip, smem);
+        Fwd<T, D, QB, NW, WPC, CAUSAL>::run_seq(Q, K, V, O, LSE, Nq, Nk, qpos, BH, ntq, c, qflip, smem);
 }
 
 // per head dimension: query blocks per wave, waves per workgroup, workgroups per CU
@@ -480,31 +483,31 @@ template <> struct Shape<128> { static constexpr int QB = 1, NW = 4, WPC = 2; };
 template <> struct Shape<256> { static constexpr int QB = 1, NW = 4, WPC = 2; };
 
 template <typename T, int D, bool CAUSAL>
-hipError_t launch16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, float c,
-                    uint32_t qflip, hipStream_t stream) {
+hipError_t launch16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Nq, int Nk,
+                    int qpos, float c, uint32_t qflip, hipStream_t stream) {
     constexpr int QB = Shape<D>::QB, NW = Shape<D>::NW, WPC = Shape<D>::WPC;
     constexpr int BM = Tile<D, QB, NW, WPC>::BM;
-    const int ntq = (N + BM - 1) / BM;
+    const int ntq = (Nq + BM - 1) / BM;
     const long long nwg = (long long)BH * ntq;
     if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((fa_fwd16_kernel<T, D, QB, NW, WPC, CAUSAL>), dim3((unsigned)nwg), dim3(64 * NW), 0, stream,
-                       (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, N, BH, ntq, c, qflip);
+                       (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, qpos, BH, ntq, c, qflip);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t dispatch16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
-                      bool causal, float c, uint32_t qflip, hipStream_t stream) {
+hipError_t dispatch16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Nq, int Nk,
+                      int qpos, int d, bool causal, float c, uint32_t qflip, hipStream_t stream) {
     switch (d) {
         case 64:
-            return causal ? launch16<T, 64, true>(q, k, v, o, lse, BH, N, c, qflip, stream)
-                          : launch16<T, 64, false>(q, k, v, o, lse, BH, N, c, qflip, stream);
+            return causal ? launch16<T, 64, true>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, stream)
+                          : launch16<T, 64, false>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, stream);
         case 128:
-            return causal ? launch16<T, 128, true>(q, k, v, o, lse, BH, N, c, qflip, stream)
-                          : launch16<T, 128, false>(q, k, v, o, lse, BH, N, c, qflip, stream);
+            return causal ? launch16<T, 128, true>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, stream)
+                          : launch16<T, 128, false>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, stream);
         case 256:
-            return causal ? launch16<T, 256, true>(q, k, v, o, lse, BH, N, c, qflip, stream)
-                          : launch16<T, 256, false>(q, k, v, o, lse, BH, N, c, qflip, stream);
+            return causal ? launch16<T, 256, true>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, stream)
+                          : launch16<T, 256, false>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, stream);
         default:
             return hipErrorNotSupported;
     }
@@ -513,9 +516,10 @@ hipError_t dispatch16(const void* q, const void* k, const void* v, void* o, floa
 }  // namespace
 
 hipError_t launch_fwd_16(bool is_bf16, const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                         int N, int d, bool causal, float c, uint32_t qflip, hipStream_t stream) {
-    return is_bf16 ? dispatch16<__bf16>(q, k, v, o, lse, BH, N, d, causal, c, qflip, stream)
-                   : dispatch16<_Float16>(q, k, v, o, lse, BH, N, d, causal, c, qflip, stream);
+                         int Nq, int Nk, int qpos, int d, bool causal, float c, uint32_t qflip,
+                         hipStream_t stream) {
+    return is_bf16 ? dispatch16<__bf16>(q, k, v, o, lse, BH, Nq, Nk, qpos, d, causal, c, qflip, stream)
+                   : dispatch16<_Float16>(q, k, v, o, lse, BH, Nq, Nk, qpos, d, causal, c, qflip, stream);
 }
 
 }  // namespace fa

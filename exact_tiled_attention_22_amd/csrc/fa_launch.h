@@ -9,10 +9,12 @@
 
 namespace fa {
 
-// 16-bit float path (bf16 or fp16): v_mfma_f32_32x32x16_{bf16,f16}.
+// 16-bit float path (bf16 or fp16): v_mfma_f32_32x32x16_{bf16,f16}.  Nq queries per head against Nk
+// keys; causal: query i sits at position qpos + i of the key sequence (qpos = 0, Nq = Nk: square).
 // c = |scale| * log2(e) (> 0), qflip = 0x80008000 to negate Q (negative scale) else 0.
 hipError_t launch_fwd_16(bool is_bf16, const void* q, const void* k, const void* v, void* o, float* lse,
-                         int BH, int N, int d, bool causal, float c, uint32_t qflip, hipStream_t stream);
+                         int BH, int Nq, int Nk, int qpos, int d, bool causal, float c, uint32_t qflip,
+                         hipStream_t stream);
 
 // float32 path: v_mfma_f32_32x32x2_f32.  c as above; qneg negates Q.
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,

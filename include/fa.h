@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
     FA_F32 = 0,      /* float32 in, float32 out */
@@ -93,6 +93,28 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int N, int d, int causal, float scale, int dtype,
               const fa_fp8_scales* s8, void* stream);
+
+/*
+ * Attention forward of Nq queries against Nk keys per (b, h): the same definition and the same tiled
+ * kernel as fa_fwd, for a query range that is not the whole key sequence.  The concept card
+ * ("FlashAttention 2 + 3 — speicherbewusste Attention-Kernels", "Kernpunkte") splits the queries into
+ * blocks that are processed independently against the streamed keys; this entry point exposes one
+ * contiguous range of those blocks.  Uses: one GPU's share of a sequence-sharded forward (queries
+ * q_start .. q_start + Nq - 1 of a sequence whose Nk keys and values are all present), and a prefill
+ * chunk appended to a key/value cache (q_start = Nk - Nq).
+ *   q, o    : DEVICE [B,H,Nq,d];  k, v : DEVICE [B,H,Nk,d];  lse : DEVICE [B,H,Nq] float32 or NULL.
+ *   causal  : 0 = every key visible (q_start must be 0; any Nq, Nk >= 1);
+ *             1 = query i sees keys j <= q_start + i; requires 0 <= q_start <= Nk - Nq.
+ *   dtype   : FA_F16 or FA_BF16 (FA_ERR_UNSUPPORTED otherwise); d : 64, 128 or 256.
+ * o must overlap none of q, k, v; lse must not overlap o.  With Nq = Nk and q_start = 0 the result is
+ * fa_fwd's, bit for bit.  The query rows a .. a + Nq - 1 of a sequence of Nk (q_start = a when causal)
+ * give fa_fwd's rows of that range bit for bit when a is a multiple of 128 and Nq a multiple of 32 (or
+ * the range ends the sequence): the kernel then puts the same rows into each wave.  Nq = 0 or B*H = 0
+ * is a no-op; Nq > 0 with Nk = 0 is FA_ERR_SHAPE.  Returns an fa_status; nothing is enqueued on error.
+ */
+int fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int Nq, int Nk, int q_start, int d, int causal, float scale, int dtype,
+                void* stream);
 
 /*
  * Block absmax quantisation to OCP e4m3fn with an optional Hadamard rotation of the head dimension
