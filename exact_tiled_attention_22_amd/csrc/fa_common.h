@@ -71,6 +71,9 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum of three floats (one v_max3_f32).
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
 // Round-to-nearest-even packing of 8 floats into the MFMA operand of type T.
 template <typename T> struct Vec;
 template <> struct Vec<__bf16> {

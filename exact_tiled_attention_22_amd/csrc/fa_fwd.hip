@@ -82,11 +82,20 @@ struct Fwd {
     // Slot s of the tile holds chunk (s % CPR) ^ swz(row) of row s / CPR.  The copies use a scalar
     // tile base and per-lane 32-bit offsets; a ragged last tile reads row N-1 in place of the missing
     // rows (they are masked or never stored), through a wave-uniform row limit.
+    // For d <= 128 a full tile takes the lane's byte offsets from foff (the same for every full tile,
+    // computed once by copy_offsets), so it costs no vector instructions; d = 256 has no registers
+    // to spare for them and recomputes the offsets.
     template <int NLOADS>
     static __device__ __forceinline__ void copy_rows(const T* __restrict__ src, int r0, int N, uint32_t lds,
-                                                     int tid, int wave) {
+                                                     int tid, int wave, const uint32_t (&foff)[NLOADS]) {
         constexpr int ROWS = NLOADS * TL::THREADS / CPR;
         const T* base = src + (size_t)r0 * D;
+        if (D <= 128 && r0 + ROWS <= N) {
+#pragma unroll
+            for (int t = 0; t < NLOADS; ++t)
+                dma16s(base, foff[t], lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
+            return;
+        }
         const int lim = min(ROWS, N - r0) - 1;  // last row of the slice inside this tile
 #pragma unroll
         for (int t = 0; t < NLOADS; ++t) {
@@ -95,6 +104,17 @@ struct Fwd {
             const int c = (slot % CPR) ^ swz<CPR>(row);
             dma16s(base, (uint32_t)((min(row, lim) * D + c * 8) * (int)sizeof(T)),
                    lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
+        }
+    }
+
+    template <int NLOADS>
+    static __device__ __forceinline__ void copy_offsets(int tid, uint32_t (&foff)[NLOADS]) {
+#pragma unroll
+        for (int t = 0; t < NLOADS; ++t) {
+            const int slot = t * TL::THREADS + tid;
+            const int row = slot / CPR;
+            const int c = (slot % CPR) ^ swz<CPR>(row);
+            foff[t] = (uint32_t)((row * D + c * 8) * (int)sizeof(T));
         }
     }
 
@@ -156,24 +176,26 @@ struct Fwd {
         bool grow = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            // 16 NKB values -> 1 as a shallow tree of 3-input maxima (short dependency chain)
+            // 16 NKB values -> 1 as a shallow tree of 3-input maxima (short dependency chain).  Every
+            // node takes three operands (a value counted twice is harmless for a maximum): a 2-input
+            // maximum of matrix results costs two extra canonicalising instructions.
             float mx;
             if constexpr (NKB == 2) {
                 float t1[11];
 #pragma unroll
                 for (int i = 0; i < 10; ++i) {
                     const int a = 3 * i, b = 3 * i + 1, d = 3 * i + 2;
-                    t1[i] = fmaxf(fmaxf(s[qb][a >> 4][a & 15], s[qb][b >> 4][b & 15]), s[qb][d >> 4][d & 15]);
+                    t1[i] = max3(s[qb][a >> 4][a & 15], s[qb][b >> 4][b & 15], s[qb][d >> 4][d & 15]);
                 }
-                t1[10] = fmaxf(s[qb][1][14], s[qb][1][15]);
-                const float t2a = fmaxf(fmaxf(t1[0], t1[1]), t1[2]), t2b = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
-                const float t2c = fmaxf(fmaxf(t1[6], t1[7]), t1[8]), t2d = fmaxf(t1[9], t1[10]);
-                mx = fmaxf(fmaxf(t2a, t2b), fmaxf(t2c, t2d));
+                t1[10] = max3(s[qb][1][14], s[qb][1][15], s[qb][0][0]);
+                const float t2a = max3(t1[0], t1[1], t1[2]), t2b = max3(t1[3], t1[4], t1[5]);
+                const float t2c = max3(t1[6], t1[7], t1[8]), t2d = max3(t1[9], t1[10], t1[0]);
+                mx = max3(max3(t2a, t2b, t2c), t2d, t2a);
             } else {
                 float t1[5];
 #pragma unroll
-                for (int i = 0; i < 5; ++i) t1[i] = fmaxf(fmaxf(s[qb][0][3 * i], s[qb][0][3 * i + 1]), s[qb][0][3 * i + 2]);
-                mx = fmaxf(fmaxf(fmaxf(t1[0], t1[1]), t1[2]), fmaxf(fmaxf(t1[3], t1[4]), s[qb][0][15]));
+                for (int i = 0; i < 5; ++i) t1[i] = max3(s[qb][0][3 * i], s[qb][0][3 * i + 1], s[qb][0][3 * i + 2]);
+                mx = max3(max3(t1[0], t1[1], t1[2]), max3(t1[3], t1[4], s[qb][0][15]), t1[0]);
             }
             mt[qb] = halves_max(mx) * c;
             grow |= mt[qb] > m_run[qb] + kTau;
@@ -316,6 +338,8 @@ struct Fwd {
             ln.vcc = (G & 1) * 2 + ((i16 & 3) >> 1);
             ln.vb = (i16 & 1) * 8;
         }
+        uint32_t foff[LPT];
+        copy_offsets<LPT>(tid, foff);
         // Q operand straight from HBM (the first iteration's wait covers these loads and the copies)
         x8 qreg[QB][KS];
 #pragma unroll
@@ -328,8 +352,8 @@ struct Fwd {
                 qreg[qb][ks] = __builtin_bit_cast(x8, raw);
             }
         }
-        copy_rows<LPT>(Kh, 0, Nk, lbase + OFF_K0, tid, wave);
-        copy_rows<LPT>(Vh, 0, Nk, lbase + OFF_V0, tid, wave);
+        copy_rows<LPT>(Kh, 0, Nk, lbase + OFF_K0, tid, wave, foff);
+        copy_rows<LPT>(Vh, 0, Nk, lbase + OFF_V0, tid, wave, foff);
         f32x16 oacc[QB][CB];
         float m_run[QB], l_run[QB];
 #pragma unroll
@@ -343,8 +367,8 @@ struct Fwd {
             wait_vmcnt<0>();
             lds_barrier();  // K_j, V_j visible; the other stage is free
             if (j + 1 < nt) {
-                copy_rows<LPT>(Kh, (j + 1) * BN, Nk, lbase + dk, tid, wave);
-                copy_rows<LPT>(Vh, (j + 1) * BN, Nk, lbase + dv, tid, wave);
+                copy_rows<LPT>(Kh, (j + 1) * BN, Nk, lbase + dk, tid, wave, foff);
+                copy_rows<LPT>(Vh, (j + 1) * BN, Nk, lbase + dv, tid, wave, foff);
             }
             if (j < ntw) {
                 f32x16 sc[QB][NKB];
@@ -396,6 +420,9 @@ struct Fwd {
             ln.vb = (i16 & 1) * 8;
         }
 
+        uint32_t foff[LPT];
+        copy_offsets<LPT>(tid, foff);
+
         // ---- prologue: Q straight into registers, K_0, V_0, K_1 into LDS, one memory latency ----
         // Q operand (B of the score MFMA): lane supplies Q[q0w + qb*32 + n32][ks*16 + h*8 + 0..7]
         x8 qreg[QB][KS];
@@ -409,9 +436,9 @@ struct Fwd {
                 qreg[qb][ks] = __builtin_bit_cast(x8, raw);
             }
         }
-        copy_rows<LPT>(Kh, 0, Nk, lbase + OFF_K0, tid, wave);
-        copy_rows<LPT>(Vh, 0, Nk, lbase + OFF_V0, tid, wave);
-        if (nt > 1) copy_rows<LPT>(Kh, BN, Nk, lbase + OFF_K1, tid, wave);
+        copy_rows<LPT>(Kh, 0, Nk, lbase + OFF_K0, tid, wave, foff);
+        copy_rows<LPT>(Vh, 0, Nk, lbase + OFF_V0, tid, wave, foff);
+        if (nt > 1) copy_rows<LPT>(Kh, BN, Nk, lbase + OFF_K1, tid, wave, foff);
         wait_vmcnt<0>();
         lds_barrier();
 
@@ -433,8 +460,8 @@ struct Fwd {
                              uint32_t dv) {
             wait_vmcnt<0>();
             lds_barrier();
-            if (j + 2 < nt) copy_rows<LPT>(Kh, (j + 2) * BN, Nk, lbase + dk, tid, wave);
-            if (j + 1 < nt) copy_rows<LPT>(Vh, (j + 1) * BN, Nk, lbase + dv, tid, wave);
+            if (j + 2 < nt) copy_rows<LPT>(Kh, (j + 2) * BN, Nk, lbase + dk, tid, wave, foff);
+            if (j + 1 < nt) copy_rows<LPT>(Vh, (j + 1) * BN, Nk, lbase + dv, tid, wave, foff);
             if (j < ntw) {
                 mask(cur, j * BN, Nk, qpos + q0w, n32, h);
                 update_max(cur, c, oacc, m_run, l_run);
