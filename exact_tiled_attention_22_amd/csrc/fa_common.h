@@ -110,6 +110,41 @@ template <> struct Vec<_Float16> {
     }
 };
 
+// ---- output staging: a wave's 32 x D output tile of 2-byte elements through LDS ----
+// The matrix accumulator leaves a lane with 4-column pieces of one row (32 rows per register), so
+// stores straight from registers would touch 32 rows with 8 bytes per lane.  Staged in the wave's own
+// LDS region (row r at r * 2D bytes, 16-byte chunk c at physical chunk c ^ ostage_swz(r)), the tile
+// leaves as whole rows: one 16-byte-per-lane store covers 64 / (D / 8) rows of contiguous output.
+// The swizzle spreads the 16 rows of one 8-byte-per-lane write, and the rows of one 16-byte read,
+// over distinct 16-byte bank groups of the 64-bank LDS.
+template <int CPR>
+__device__ __forceinline__ int ostage_swz(int row) {
+    if constexpr (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// Lane (row n32, half h) writes its 4 elements of columns 8 * chunk + 4 * h + 0..3.
+template <int D, typename X4>
+__device__ __forceinline__ void ostage_put(char* wl, int n32, int h, int chunk, const X4& val) {
+    static_assert(sizeof(X4) == 8, "four 2-byte elements");
+    *(X4*)(wl + n32 * (2 * D) + (chunk ^ ostage_swz<D / 8>(n32)) * 16 + h * 8) = val;
+}
+
+// After every lane of the wave has put its pieces: rows row0 + r (r < 32, row0 + r < nrows) of dst.
+template <typename T, int D>
+__device__ __forceinline__ void ostage_flush(T* __restrict__ dst, int row0, int nrows, const char* wl, int lane) {
+    constexpr int CPR = D / 8, RPS = 64 / CPR;
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    // the wave's own LDS writes land before its lanes read each other's rows back
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 32 / RPS; ++i) {
+        const int r = i * RPS + lane / CPR, c = lane % CPR;
+        const i32x4_t val = *(const i32x4_t*)(wl + r * (2 * D) + (c ^ ostage_swz<CPR>(r)) * 16);
+        if (row0 + r < nrows) *(i32x4_t*)(dst + (size_t)(row0 + r) * D + c * 8) = val;
+    }
+}
+
 // Work partition: block id -> (head slice bh, query tile qt).
 // Consecutive block ids are dispatched round-robin over the 8 XCDs (each with its own L2), so when
 // B*H is a multiple of 8 every XCD is given whole heads: all query tiles of a head then read that

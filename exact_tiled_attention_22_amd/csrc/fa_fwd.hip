@@ -51,6 +51,7 @@ struct Tile {
     static_assert(CHUNKS % THREADS == 0, "tiles split evenly over threads");
     static_assert(LDS_BYTES <= LDS_LIMIT, "LDS budget");
     static_assert(LPT <= 16, "vmcnt range");
+    static_assert(D > 128 || BM * D * 2 <= LDS_BYTES, "output staging fits the K/V stages");
 };
 
 // XOR swizzle of the 16-byte chunk index inside one LDS row.  The LDS serves 256 bytes per clock
@@ -278,11 +279,44 @@ struct Fwd {
         }
     }
 
-    // O = acc / l rounded to T (lane holds 16 columns of its query per 32-column block), and
-    // lse = ln2 * (m + log2 l)
+    // O = acc / l rounded to T, and lse = ln2 * (m + log2 l).  The tile goes out through this wave's
+    // LDS region as whole rows (ostage_put / ostage_flush); the caller has passed a workgroup barrier
+    // after the last tile, so every LDS stage is free.
     static __device__ __forceinline__ void epilogue(T* __restrict__ O, float* __restrict__ LSE, size_t head, int bh,
-                                                    int Nq, int q0w, int n32, int h, const f32x16 (&oacc)[QB][CB],
-                                                    const float (&m_run)[QB], const float (&l_run)[QB]) {
+                                                    int Nq, int q0w, int lane, char* wl,
+                                                    const f32x16 (&oacc)[QB][CB], const float (&m_run)[QB],
+                                                    const float (&l_run)[QB]) {
+        const int n32 = lane & 31, h = lane >> 5;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float lt = halves_sum(l_run[qb]);
+            const float inv = 1.0f / lt;
+            char* tile = wl + qb * 32 * D * (int)sizeof(T);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    x4 out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = (T)(oacc[qb][cb][g * 4 + e] * inv);
+                    ostage_put<D>(tile, n32, h, cb * 4 + g, out);
+                }
+            if (LSE != nullptr && h == 0) {
+                const int query = q0w + qb * 32 + n32;
+                if (query < Nq) LSE[(size_t)bh * Nq + query] = (m_run[qb] + __log2f(lt)) * 0.69314718055994531f;
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            ostage_flush<T, D>(O + head, q0w + qb * 32, Nq, wl + qb * 32 * D * (int)sizeof(T), lane);
+    }
+
+    // The same output written straight from registers (8 bytes per lane and store, 32 rows per
+    // store); d = 256 keeps it: staging its 512-byte rows measured slower there.
+    static __device__ __forceinline__ void epilogue_direct(T* __restrict__ O, float* __restrict__ LSE, size_t head,
+                                                           int bh, int Nq, int q0w, int n32, int h,
+                                                           const f32x16 (&oacc)[QB][CB], const float (&m_run)[QB],
+                                                           const float (&l_run)[QB]) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const float lt = halves_sum(l_run[qb]);
@@ -384,7 +418,7 @@ struct Fwd {
             iteration(j, OFF_K0, OFF_V0, OFF_K1, OFF_V1);
             if (j + 1 < nt) iteration(j + 1, OFF_K1, OFF_V1, OFF_K0, OFF_V0);
         }
-        epilogue(O, LSE, head, bh, Nq, q0w, n32, h, oacc, m_run, l_run);
+        epilogue_direct(O, LSE, head, bh, Nq, q0w, n32, h, oacc, m_run, l_run);
     }
 
     static __device__ __forceinline__ void run(const T* __restrict__ Q, const T* __restrict__ K,
@@ -486,7 +520,8 @@ struct Fwd {
             if (j + 1 < nt) iteration(j + 1, s1, s0, OFF_K0, OFF_V1, OFF_K1, OFF_V0);
         }
 
-        epilogue(O, LSE, head, bh, Nq, q0w, n32, h, oacc, m_run, l_run);
+        lds_barrier();  // every wave is past its last LDS read: the stages become output staging
+        epilogue(O, LSE, head, bh, Nq, q0w, lane, smem + wave * QW * D * (int)sizeof(T), oacc, m_run, l_run);
     }
 };
 

@@ -57,6 +57,7 @@ struct Tile8 {
     static constexpr int LDS_BYTES = 4 * KV_BYTES + Q_BYTES;
     static_assert(LPT >= 1 && CHUNKS % THREADS == 0 && Q_CHUNKS % THREADS == 0, "tiles split evenly");
     static_assert(LDS_BYTES <= 160 * 1024 / WPC, "LDS budget");
+    static_assert(BM * D * 2 <= LDS_BYTES, "bf16 output staging fits the workgroup's LDS");
 };
 
 // chunk swizzle of an LDS row (128- or 256-byte rows: 3 bits; 64-byte rows: 2 bits).  Rows read
@@ -272,22 +273,25 @@ struct Fwd8 {
             if (j + 1 < nt) iteration(j + 1, s1, s0, TL::OFF_K0, TL::OFF_V1, TL::OFF_K1, TL::OFF_V0);
         }
 
+        // the output leaves through this wave's LDS region as whole rows (every stage is free once
+        // all waves are past their last tile)
+        lds_barrier();
+        char* wl = smem + wave * QW * D * 2;
         const float lt = halves_sum(l_run);
         const float inv = svmax / (64.0f * lt);  // undo the 2^kBoost8 carried by p~
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = (__bf16)(oacc[cb][g * 4 + e] * inv);
+                ostage_put<D>(wl, n32, h, cb * 4 + g, out);
+            }
         const int query = q0w + n32;
-        if (query < N) {
-            __bf16* orow = O + head + (size_t)query * D;
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    bf16x4 out;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) out[e] = (__bf16)(oacc[cb][g * 4 + e] * inv);
-                    *(bf16x4*)(orow + cb * 32 + g * 8 + h * 4) = out;
-                }
-            if (LSE != nullptr && h == 0) LSE[(size_t)bh * N + query] = (m_run + __log2f(lt)) * 0.69314718055994531f;
-        }
+        if (LSE != nullptr && h == 0 && query < N)
+            LSE[(size_t)bh * N + query] = (m_run + __log2f(lt)) * 0.69314718055994531f;
+        ostage_flush<__bf16, D>(O + head, q0w, N, wl, lane);
     }
 };
 
