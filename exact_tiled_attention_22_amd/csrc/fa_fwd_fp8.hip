@@ -200,7 +200,7 @@ struct Fwd8 {
                 cj *= SK[srow + j];
                 const float rv = SV[srow + j] * inv_svmax;  // sv[j] / svmax in (0, 1]
                 delta += __log2f(rv);
-                lscale /= rv;
+                lscale *= __builtin_amdgcn_rcpf(rv);  // hardware reciprocal (1 ulp): a row-sum factor
             }
             // mask
             if ((kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > q0w)) {
@@ -215,11 +215,18 @@ struct Fwd8 {
             }
             // running maximum with lazy correction
             {
-                float mx = fmaxf(cur[0][0], cur[1][0]);
+                // 32 values -> 1 through 3-input maxima only (a value counted twice is harmless; a
+                // 2-input maximum of matrix results costs two extra canonicalising instructions)
+                float t1[11];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
+                for (int i = 0; i < 10; ++i) {
+                    const int a = 3 * i, b = 3 * i + 1, e = 3 * i + 2;
+                    t1[i] = max3(cur[a >> 4][a & 15], cur[b >> 4][b & 15], cur[e >> 4][e & 15]);
+                }
+                t1[10] = max3(cur[1][14], cur[1][15], cur[0][0]);
+                const float t2a = max3(t1[0], t1[1], t1[2]), t2b = max3(t1[3], t1[4], t1[5]);
+                const float t2c = max3(t1[6], t1[7], t1[8]), t2d = max3(t1[9], t1[10], t1[0]);
+                const float mx = max3(max3(t2a, t2b, t2c), t2d, t2a);
                 const float mt = halves_max(mx) * cj;
                 if (__ballot(mt > m_run + kTau8)) {
                     const float mn = fmaxf(m_run, mt);
