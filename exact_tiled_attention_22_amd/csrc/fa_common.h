@@ -134,14 +134,13 @@ __device__ __forceinline__ void ostage_put(char* wl, int n32, int h, int chunk, 
 template <typename T, int D>
 __device__ __forceinline__ void ostage_flush(T* __restrict__ dst, int row0, int nrows, const char* wl, int lane) {
     constexpr int CPR = D / 8, RPS = 64 / CPR;
-    typedef int i32x4_t __attribute__((ext_vector_type(4)));
     // the wave's own LDS writes land before its lanes read each other's rows back
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int i = 0; i < 32 / RPS; ++i) {
         const int r = i * RPS + lane / CPR, c = lane % CPR;
-        const i32x4_t val = *(const i32x4_t*)(wl + r * (2 * D) + (c ^ ostage_swz<CPR>(r)) * 16);
-        if (row0 + r < nrows) *(i32x4_t*)(dst + (size_t)(row0 + r) * D + c * 8) = val;
+        const i32x4 val = *(const i32x4*)(wl + r * (2 * D) + (c ^ ostage_swz<CPR>(r)) * 16);
+        if (row0 + r < nrows) *(i32x4*)(dst + (size_t)(row0 + r) * D + c * 8) = val;
     }
 }
 
