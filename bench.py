@@ -265,7 +265,10 @@ def bench_decode(args) -> int:
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,1), resident in HBM)",
         "config": {"workload": f"bf16 decode B8 H32 Nq{c['Nq']} Nk32768 d128 non-causal", **c, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("decode_vec_kernel" if c["Nq"] == 1 else "decode_split_kernel")
+                     + " + decode_merge_kernel (the launches of one fa_fwd_decode call)",
+                     "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(achieved / 8000.0, 4), "traffic": None, "kernel_avg_ms": round(avg_ms, 5)},
     }
     if not args.no_cpu_baseline:
