@@ -277,6 +277,78 @@ def bench_decode(args) -> int:
     return 0
 
 
+def bench_shard(args, w) -> int:
+    """One GPU's share of a sequence-sharded causal forward: with the query rows cut into G equal ranges
+    (rank r owns rows [r*N/G, (r+1)*N/G)) and K/V gathered on every GPU, rank r attends its rows to the
+    keys they can see, [0, (r+1)*N/G).  A share has only B*H*N/(G*128) query tiles, too few workgroups
+    to fill the GPU, so it runs through fa_fwd_split with each query tile's keys cut into enough shares
+    for about two workgroups per CU (fa_fwd_rect, unsplit, is timed beside it).  Every rank's share is
+    timed on this one GPU (HIP events, median); the line reports the heaviest share (the last rank),
+    which sets the step time of the sharded forward.  Flops per share follow the metric's convention:
+    4*B*H*d*(Nq*q_start + Nq^2/2), which sums over the ranks to the workload's 4*B*H*N^2*d/2."""
+    import torch
+
+    import exact_tiled_attention_22_amd as fa
+    from synth import gen_qkv
+
+    G = args.shard
+    if not w.causal or w.dtype not in ("bf16", "f16") or G < 2 or w.N % G:
+        print(f"--shard needs a causal 16-bit workload whose N divides by G (workload {w.cfg_id}, G {G})",
+              file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    q, k, v = (t.to(dev) for t in gen_qkv(w.B, w.H, w.N, w.d, w.dtype, w.cfg_id))
+    nq = w.N // G
+    base_wg = w.B * w.H * ((nq + 127) // 128)
+    nsplit = max(1, min(64, -(-2 * cus // base_wg)))
+    ws = torch.empty(fa.split_workspace_bytes(w.B, w.H, nq, w.d, nsplit), dtype=torch.uint8, device=dev)
+    shares = []
+    for r in range(G):
+        q0, nk = r * nq, (r + 1) * nq
+        qr = q[:, :, q0:q0 + nq].contiguous()
+        kr, vr = k[:, :, :nk].contiguous(), v[:, :, :nk].contiguous()
+        o = torch.empty_like(qr)
+        lse = torch.empty((w.B, w.H, nq), dtype=torch.float32, device=dev)
+
+        def split_step(qr=qr, kr=kr, vr=vr, o=o, lse=lse, q0=q0):
+            return fa.fwd_split(qr, kr, vr, nsplit=nsplit, causal=True, q_start=q0, scale=w.scale, out=o, lse=lse,
+                                workspace=ws)
+
+        def rect_step(qr=qr, kr=kr, vr=vr, o=o, lse=lse, q0=q0):
+            return fa.fwd_rect(qr, kr, vr, causal=True, q_start=q0, scale=w.scale, out=o, lse=lse)
+
+        flops = 4.0 * w.B * w.H * w.d * (nq * q0 + nq * nq / 2.0)
+        row = {"rank": r, "q_rows": [q0, q0 + nq], "keys": nk}
+        for name, step in (("split", split_step), ("rect", rect_step)):
+            for _ in range(args.warmup):
+                step()
+            st = launch_stats(step, args.steps, dev)
+            row[f"{name}_median_ms"] = round(st["median"], 5)
+            row[f"{name}_tflops"] = round(flops / (st["median"] * 1e-3) / 1e12, 2)
+        shares.append(row)
+        del qr, kr, vr, o, lse
+    top = shares[-1]
+    line = {
+        "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, /2 causal; one GPU's share of a sequence split)",
+        "value": top["split_tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": top["split_median_ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0,1), resident in HBM)",
+        "config": {"workload": f"{w.name}: query rows {top['q_rows'][0]}..{top['q_rows'][1] - 1} of a {G}-way "
+                               f"sequence split against keys 0..{top['keys'] - 1} (one GPU's share, fa_fwd_split "
+                               f"with {nsplit} key shares per query tile)",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": True, "shards": G, "key_shares": nsplit,
+                   "parallelism": "single GPU", "shares": shares},
+        "roofline": {"bound": "mfma", "kernel": "fa_fwd16_kernel (key shares) + decode_merge_kernel",
+                     "achieved": top["split_tflops"], "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                     "frac": round(top["split_tflops"] / PEAK_TFLOPS[w.dtype], 4), "traffic": None,
+                     "kernel_median_ms": top["split_median_ms"]},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def decode_cpu_baseline(c, budget_s: float = 10.0):
     """The float64 oracle (attention_rect: full score rows) on whole (b, h) heads of the decode workload
     until ~budget_s, in the same unit: K/V cache bytes (2 * Nk * d * 2 per head) per second."""
@@ -408,6 +480,8 @@ def main() -> int:
                     help="time the unfused path (S and P through HBM) and the fused kernel beside it")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (dQ, dK, dV from the saved lse) instead of the forward")
+    ap.add_argument("--shard", type=int, default=0, metavar="G",
+                    help="time one GPU's share of a G-way sequence-sharded causal forward (workload 3 or 4)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -432,6 +506,8 @@ def main() -> int:
     w = CONFIGS[args.config]
     if args.naive:
         return bench_naive(args, w)
+    if args.shard:
+        return bench_shard(args, w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     seed = w.cfg_id

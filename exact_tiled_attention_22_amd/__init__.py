@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     fwd_decode,
     fwd_naive,
     fwd_rect,
+    fwd_split,
     last_error,
     lib,
     naive_pv,
@@ -26,5 +27,6 @@ from .binding import (  # noqa: F401
     naive_scores,
     naive_softmax,
     naive_workspace_bytes,
+    split_workspace_bytes,
     status_str,
 )

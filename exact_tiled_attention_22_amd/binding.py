@@ -60,6 +60,10 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd.restype = i
     L.fa_fwd_rect.argtypes = [vp] * 5 + [i] * 7 + [f, i, vp]
     L.fa_fwd_rect.restype = i
+    L.fa_fwd_split.argtypes = [vp] * 5 + [i] * 7 + [f, i, i, vp, ctypes.c_size_t, vp]
+    L.fa_fwd_split.restype = i
+    L.fa_fwd_split_workspace_bytes.argtypes = [i] * 5
+    L.fa_fwd_split_workspace_bytes.restype = ctypes.c_size_t
     L.fa_fwd_decode.argtypes = [vp] * 5 + [i] * 6 + [f, i, vp, ctypes.c_size_t, vp]
     L.fa_fwd_decode.restype = i
     L.fa_decode_workspace_bytes.argtypes = [i] * 5
@@ -195,6 +199,37 @@ def fwd_rect(q, k, v, *, causal: bool = False, q_start: int | None = None, scale
     st = lib().fa_fwd_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, int(q_start), d,
                            int(bool(causal)), float(scale), DTYPE_CODE[q.dtype], _stream(q.device))
     _check(st, "fa_fwd_rect")
+    return out, lse
+
+
+def split_workspace_bytes(B: int, H: int, Nq: int, d: int, nsplit: int) -> int:
+    return int(lib().fa_fwd_split_workspace_bytes(B, H, Nq, d, nsplit))
+
+
+def fwd_split(q, k, v, *, nsplit: int, causal: bool = False, q_start: int | None = None, scale: float | None = None,
+              out=None, lse=None, workspace=None):
+    """fwd_rect with each query tile's keys split into `nsplit` shares merged afterwards (fa_fwd_split).
+    `workspace`: a uint8 GPU tensor of at least split_workspace_bytes(...) bytes (allocated here if None).
+    Returns (o, lse)."""
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v must be contiguous 4-D GPU tensors")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must be [B, H, Nk, d] of q's dtype")
+    if q_start is None:
+        q_start = Nk - Nq if causal else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = _out(out, q.shape, q.dtype, q.device, "out")
+    lse = _out(lse, (B, H, Nq), torch.float32, q.device, "lse")
+    need = split_workspace_bytes(B, H, Nq, d, nsplit) if nsplit >= 1 else 0
+    ws = _workspace(workspace, need, q.device)
+    st = lib().fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, int(q_start), d,
+                            int(bool(causal)), float(scale), DTYPE_CODE[q.dtype], int(nsplit), _ptr(ws),
+                            ws.numel() if ws is not None else 0, _stream(q.device))
+    _check(st, "fa_fwd_split")
     return out, lse
 
 

@@ -12,6 +12,8 @@
 //      which is the same softmax over the union of the chunks.
 // The waves share nothing, so there is no workgroup barrier; each waits only for its own copies.
 // Causal: query i (of Nq) sees keys j <= i + Nk - Nq (the queries are the last Nq positions).
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -396,6 +398,25 @@ hipError_t launch_decode_dt(const void* q, const void* k, const void* v, void* o
 }
 
 }  // namespace
+
+hipError_t launch_merge_partials(bool is_bf16, const float* Op, const float* Lp, void* o, float* lse, int BH, int Nq,
+                                 int nc, int d, hipStream_t stream) {
+    const long long nm = (long long)BH * Nq;
+    if (nm > 0x7fffffffLL) return hipErrorInvalidValue;
+    auto go = [&](auto tag, auto dim) -> hipError_t {
+        using T = decltype(tag);
+        constexpr int D = decltype(dim)::value;
+        hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)nm), dim3(D), 0, stream, Op, Lp, (T*)o, lse, Nq,
+                           nc);
+        return hipGetLastError();
+    };
+    switch (d) {
+        case 64: return is_bf16 ? go(__bf16{}, std::integral_constant<int, 64>{}) : go(_Float16{}, std::integral_constant<int, 64>{});
+        case 128: return is_bf16 ? go(__bf16{}, std::integral_constant<int, 128>{}) : go(_Float16{}, std::integral_constant<int, 128>{});
+        case 256: return is_bf16 ? go(__bf16{}, std::integral_constant<int, 256>{}) : go(_Float16{}, std::integral_constant<int, 256>{});
+        default: return hipErrorNotSupported;
+    }
+}
 
 hipError_t launch_decode_16(bool is_bf16, const void* q, const void* k, const void* v, void* o, float* lse, float* work,
                             int BH, int Nq, int Nk, int d, bool causal, int nsplit, int chunk, float c, uint32_t qflip,

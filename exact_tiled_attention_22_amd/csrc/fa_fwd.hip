@@ -67,7 +67,16 @@ __device__ __forceinline__ int swz(int row) {
     else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
-template <typename T, int D, int QB, int NW, int WPC, bool CAUSAL>
+// Key split (SPLIT): the workgroups of one query tile each take a contiguous share of its key tiles and
+// write a partial result (O normalised over the share, float32, and lse in base 2; an empty share gives
+// O = 0 and lse = -inf) that a second launch merges.  n = shares per query tile.
+struct SplitOut {
+    int n;
+    float* Op;  // [BH, n, Nq, D]
+    float* Lp;  // [BH, n, Nq]
+};
+
+template <typename T, int D, int QB, int NW, int WPC, bool CAUSAL, bool SPLIT>
 struct Fwd {
     using TL = Tile<D, QB, NW, WPC>;
     using VT = Vec<T>;
@@ -205,7 +214,8 @@ struct Fwd {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const float mn = fmaxf(m_run[qb], mt[qb]);
-                const float alpha = fast_exp2(m_run[qb] - mn);
+                // a key share can leave a row without any visible key so far (m = -inf on both sides)
+                const float alpha = (SPLIT && m_run[qb] == mn) ? 1.0f : fast_exp2(m_run[qb] - mn);
                 m_run[qb] = mn;
                 l_run[qb] *= alpha;
 #pragma unroll
@@ -219,7 +229,8 @@ struct Fwd {
                                                 float (&l_run)[QB], x8 (&p)[QB][2 * NKB]) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const float negm = -m_run[qb];
+            // a row with no visible key in its share keeps m = -inf: its probabilities are 0, not NaN
+            const float negm = (SPLIT && m_run[qb] == -INFINITY) ? 0.0f : -m_run[qb];
             float part[2 * NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -339,21 +350,84 @@ struct Fwd {
         }
     }
 
+    // Partial result of a key share: O_s = acc / l (float32) and lse_s = m + log2 l (base 2), or O_s = 0
+    // and lse_s = -inf for a row that saw no key of its share.
+    static __device__ __forceinline__ void epilogue_split(const SplitOut& so, int split, int bh, int Nq, int q0w,
+                                                          int n32, int h, const f32x16 (&oacc)[QB][CB],
+                                                          const float (&m_run)[QB], const float (&l_run)[QB]) {
+        const size_t part = (size_t)bh * so.n + split;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float lt = halves_sum(l_run[qb]);
+            const bool empty = lt == 0.0f;
+            const float inv = empty ? 0.0f : 1.0f / lt;
+            const int query = q0w + qb * 32 + n32;
+            if (query < Nq) {
+                float* orow = so.Op + (part * Nq + query) * D;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        f32x4 out;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) out[e] = oacc[qb][cb][g * 4 + e] * inv;
+                        *(f32x4*)(orow + cb * 32 + g * 8 + h * 4) = out;
+                    }
+                if (h == 0) so.Lp[part * Nq + query] = empty ? -INFINITY : m_run[qb] + __log2f(lt);
+            }
+        }
+    }
+
+    // Rows of an empty key share: O_s = 0, lse_s = -inf.
+    static __device__ __forceinline__ void empty_split(const SplitOut& so, int split, int bh, int Nq, int q0) {
+        const size_t part = (size_t)bh * so.n + split;
+        for (int i = threadIdx.x; i < BM * D / 4; i += TL::THREADS) {
+            const int row = i / (D / 4), col = (i % (D / 4)) * 4;
+            if (q0 + row < Nq) *(f32x4*)(so.Op + (part * Nq + q0 + row) * D + col) = f32x4{};
+        }
+        for (int row = threadIdx.x; row < BM; row += TL::THREADS)
+            if (q0 + row < Nq) so.Lp[part * Nq + q0 + row] = -INFINITY;
+    }
+
+    // Key tiles [jb, je) of this workgroup: all of them, or its share when SPLIT.
+    static __device__ __forceinline__ void tile_range(int nt, int split, int nsplit, int& jb, int& je) {
+        jb = 0;
+        je = nt;
+        if constexpr (SPLIT) {
+            const int per = (nt + nsplit - 1) / nsplit;
+            jb = min(nt, split * per);
+            je = min(nt, jb + per);
+        }
+    }
+
+    // Block id -> (bh, query tile, key share); the shares of a query tile sit nbase ids apart, so with
+    // nbase a multiple of 8 they run on the same XCD (L2) as the unsplit tile would.
+    static __device__ __forceinline__ void locate(int BH, int ntq, int nsplit, int& bh, int& qt, int& split) {
+        int bid = blockIdx.x;
+        split = 0;
+        if constexpr (SPLIT) {
+            const int nbase = BH * ntq;
+            split = bid / nbase;
+            bid -= split * nbase;
+        }
+        map_block(bid, BH, ntq, CAUSAL, bh, qt);
+    }
+
     // In-order pipeline for large head dimensions (one score buffer): iteration j holds K_j and V_j
     // in stage j % 2 and copies K_{j+1}, V_{j+1} into the other stage; the scores of tile j come first,
     // then its softmax, whose exponentials interleave with the value MFMAs.
     static __device__ __forceinline__ void run_seq(const T* __restrict__ Q, const T* __restrict__ K,
                                                    const T* __restrict__ V, T* __restrict__ O,
                                                    float* __restrict__ LSE, int Nq, int Nk, int qpos, int BH,
-                                                   int ntq, float c, uint32_t qflip, char* smem) {
+                                                   int ntq, float c, uint32_t qflip, char* smem, SplitOut so) {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int n32 = lane & 31;
         const int h = lane >> 5;
         const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-        int bh, qt;
-        map_block(blockIdx.x, BH, ntq, CAUSAL, bh, qt);
+        int bh, qt, split;
+        locate(BH, ntq, so.n, bh, qt, split);
         const size_t head = (size_t)bh * Nq * D;  // Q, O
         const size_t headk = (size_t)bh * Nk * D; // K, V
         const T* Qh = Q + head;
@@ -361,8 +435,14 @@ struct Fwd {
         const T* Vh = V + headk;
         const int q0 = qt * BM;
         const int q0w = q0 + wave * QW;
-        const int nt = ((CAUSAL ? min(Nk, qpos + q0 + BM) : Nk) + BN - 1) / BN;
-        const int ntw = ((CAUSAL ? min(Nk, qpos + q0w + QW) : Nk) + BN - 1) / BN;
+        int jb, je;  // key tiles of this workgroup (its share when split)
+        tile_range(((CAUSAL ? min(Nk, qpos + q0 + BM) : Nk) + BN - 1) / BN, split, so.n, jb, je);
+        if (SPLIT && jb >= je) {
+            empty_split(so, split, bh, Nq, q0);
+            return;
+        }
+        // tiles this wave computes: [jb, ntw)
+        const int ntw = min(je, ((CAUSAL ? min(Nk, qpos + q0w + QW) : Nk) + BN - 1) / BN);
         Lane ln;
         ln.kperm = ((n32 >> 4) & 1) * 16 + ((n32 >> 2) & 1) * 8 + ((n32 >> 3) & 1) * 4 + (n32 & 3);
         ln.h = h;
@@ -386,8 +466,8 @@ struct Fwd {
                 qreg[qb][ks] = __builtin_bit_cast(x8, raw);
             }
         }
-        copy_rows<LPT>(Kh, 0, Nk, lbase + OFF_K0, tid, wave, foff);
-        copy_rows<LPT>(Vh, 0, Nk, lbase + OFF_V0, tid, wave, foff);
+        copy_rows<LPT>(Kh, jb * BN, Nk, lbase + OFF_K0, tid, wave, foff);
+        copy_rows<LPT>(Vh, jb * BN, Nk, lbase + OFF_V0, tid, wave, foff);
         f32x16 oacc[QB][CB];
         float m_run[QB], l_run[QB];
 #pragma unroll
@@ -400,7 +480,7 @@ struct Fwd {
         auto iteration = [&](int j, int ok, int ov, uint32_t dk, uint32_t dv) {
             wait_vmcnt<0>();
             lds_barrier();  // K_j, V_j visible; the other stage is free
-            if (j + 1 < nt) {
+            if (j + 1 < je) {
                 copy_rows<LPT>(Kh, (j + 1) * BN, Nk, lbase + dk, tid, wave, foff);
                 copy_rows<LPT>(Vh, (j + 1) * BN, Nk, lbase + dv, tid, wave, foff);
             }
@@ -414,17 +494,20 @@ struct Fwd {
                 pv(smem + ov, p, oacc, ln);
             }
         };
-        for (int j = 0; j < nt; j += 2) {
+        for (int j = jb; j < je; j += 2) {
             iteration(j, OFF_K0, OFF_V0, OFF_K1, OFF_V1);
-            if (j + 1 < nt) iteration(j + 1, OFF_K1, OFF_V1, OFF_K0, OFF_V0);
+            if (j + 1 < je) iteration(j + 1, OFF_K1, OFF_V1, OFF_K0, OFF_V0);
         }
-        epilogue_direct(O, LSE, head, bh, Nq, q0w, n32, h, oacc, m_run, l_run);
+        if constexpr (SPLIT)
+            epilogue_split(so, split, bh, Nq, q0w, n32, h, oacc, m_run, l_run);
+        else
+            epilogue_direct(O, LSE, head, bh, Nq, q0w, n32, h, oacc, m_run, l_run);
     }
 
     static __device__ __forceinline__ void run(const T* __restrict__ Q, const T* __restrict__ K,
                                                const T* __restrict__ V, T* __restrict__ O,
                                                float* __restrict__ LSE, int Nq, int Nk, int qpos, int BH,
-                                               int ntq, float c, uint32_t qflip, char* smem) {
+                                               int ntq, float c, uint32_t qflip, char* smem, SplitOut so) {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -432,8 +515,8 @@ struct Fwd {
         const int h = lane >> 5;
         const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
-        int bh, qt;
-        map_block(blockIdx.x, BH, ntq, CAUSAL, bh, qt);
+        int bh, qt, split;
+        locate(BH, ntq, so.n, bh, qt, split);
         const size_t head = (size_t)bh * Nq * D;  // Q, O
         const size_t headk = (size_t)bh * Nk * D; // K, V
         const T* Qh = Q + head;
@@ -441,8 +524,14 @@ struct Fwd {
         const T* Vh = V + headk;
         const int q0 = qt * BM;
         const int q0w = q0 + wave * QW;
-        const int nt = ((CAUSAL ? min(Nk, qpos + q0 + BM) : Nk) + BN - 1) / BN;   // tiles of the workgroup
-        const int ntw = ((CAUSAL ? min(Nk, qpos + q0w + QW) : Nk) + BN - 1) / BN; // tiles this wave computes
+        int jb, je;  // key tiles of the workgroup (its share when split)
+        tile_range(((CAUSAL ? min(Nk, qpos + q0 + BM) : Nk) + BN - 1) / BN, split, so.n, jb, je);
+        if (SPLIT && jb >= je) {
+            empty_split(so, split, bh, Nq, q0);
+            return;
+        }
+        // tiles this wave computes: [jb, ntw)
+        const int ntw = min(je, ((CAUSAL ? min(Nk, qpos + q0w + QW) : Nk) + BN - 1) / BN);
 
         Lane ln;
         ln.kperm = ((n32 >> 4) & 1) * 16 + ((n32 >> 2) & 1) * 8 + ((n32 >> 3) & 1) * 4 + (n32 & 3);
@@ -470,9 +559,9 @@ struct Fwd {
                 qreg[qb][ks] = __builtin_bit_cast(x8, raw);
             }
         }
-        copy_rows<LPT>(Kh, 0, Nk, lbase + OFF_K0, tid, wave, foff);
-        copy_rows<LPT>(Vh, 0, Nk, lbase + OFF_V0, tid, wave, foff);
-        if (nt > 1) copy_rows<LPT>(Kh, BN, Nk, lbase + OFF_K1, tid, wave, foff);
+        copy_rows<LPT>(Kh, jb * BN, Nk, lbase + OFF_K0, tid, wave, foff);
+        copy_rows<LPT>(Vh, jb * BN, Nk, lbase + OFF_V0, tid, wave, foff);
+        if (jb + 1 < je) copy_rows<LPT>(Kh, (jb + 1) * BN, Nk, lbase + OFF_K1, tid, wave, foff);
         wait_vmcnt<0>();
         lds_barrier();
 
@@ -494,8 +583,8 @@ struct Fwd {
                              uint32_t dv) {
             wait_vmcnt<0>();
             lds_barrier();
-            if (j + 2 < nt) copy_rows<LPT>(Kh, (j + 2) * BN, Nk, lbase + dk, tid, wave, foff);
-            if (j + 1 < nt) copy_rows<LPT>(Vh, (j + 1) * BN, Nk, lbase + dv, tid, wave, foff);
+            if (j + 2 < je) copy_rows<LPT>(Kh, (j + 2) * BN, Nk, lbase + dk, tid, wave, foff);
+            if (j + 1 < je) copy_rows<LPT>(Vh, (j + 1) * BN, Nk, lbase + dv, tid, wave, foff);
             if (j < ntw) {
                 mask(cur, j * BN, Nk, qpos + q0w, n32, h);
                 update_max(cur, c, oacc, m_run, l_run);
@@ -514,28 +603,32 @@ struct Fwd {
                 __builtin_amdgcn_s_setprio(0);
             }
         };
-        for (int j = 0; j < nt; j += 2) {
-            // even j: K_{j+1} in stage 1, V_j in stage 0; copies K_{j+2} -> stage 0, V_{j+1} -> stage 1
+        for (int j = jb; j < je; j += 2) {
+            // j - jb even: K_{j+1} in stage 1, V_j in stage 0; copies K_{j+2} -> stage 0, V_{j+1} -> stage 1
             iteration(j, s0, s1, OFF_K1, OFF_V0, OFF_K0, OFF_V1);
-            if (j + 1 < nt) iteration(j + 1, s1, s0, OFF_K0, OFF_V1, OFF_K1, OFF_V0);
+            if (j + 1 < je) iteration(j + 1, s1, s0, OFF_K0, OFF_V1, OFF_K1, OFF_V0);
         }
 
-        lds_barrier();  // every wave is past its last LDS read: the stages become output staging
-        epilogue(O, LSE, head, bh, Nq, q0w, lane, smem + wave * QW * D * (int)sizeof(T), oacc, m_run, l_run);
+        if constexpr (SPLIT) {
+            epilogue_split(so, split, bh, Nq, q0w, n32, h, oacc, m_run, l_run);
+        } else {
+            lds_barrier();  // every wave is past its last LDS read: the stages become output staging
+            epilogue(O, LSE, head, bh, Nq, q0w, lane, smem + wave * QW * D * (int)sizeof(T), oacc, m_run, l_run);
+        }
     }
 };
 
-// One workgroup per (b, h, query tile); WPC of them share a CU (2 waves per SIMD in total), so one
-// workgroup's prologue and epilogue overlap the other's tile loop.
-template <typename T, int D, int QB, int NW, int WPC, bool CAUSAL>
+// One workgroup per (b, h, query tile) (and key share when SPLIT); WPC of them share a CU (2 waves per
+// SIMD in total), so one workgroup's prologue and epilogue overlap the other's tile loop.
+template <typename T, int D, int QB, int NW, int WPC, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(64 * NW, (NW * WPC) / 4) void fa_fwd16_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
-    float* __restrict__ LSE, int Nq, int Nk, int qpos, int BH, int ntq, float c, uint32_t qflip) {
+    float* __restrict__ LSE, int Nq, int Nk, int qpos, int BH, int ntq, float c, uint32_t qflip, SplitOut so) {
     __shared__ __attribute__((aligned(1024))) char smem[Tile<D, QB, NW, WPC>::LDS_BYTES];
     if constexpr (D <= 128)
-        Fwd<T, D, QB, NW, WPC, CAUSAL>::run(Q, K, V, O, LSE, Nq, Nk, qpos, BH, ntq, c, qflip, smem);
+        Fwd<T, D, QB, NW, WPC, CAUSAL, SPLIT>::run(Q, K, V, O, LSE, Nq, Nk, qpos, BH, ntq, c, qflip, smem, so);
     else
-        Fwd<T, D, QB, NW, WPC, CAUSAL>::run_seq(Q, K, V, O, LSE, Nq, Nk, qpos, BH, ntq, c, qflip, smem);
+        Fwd<T, D, QB, NW, WPC, CAUSAL, SPLIT>::run_seq(Q, K, V, O, LSE, Nq, Nk, qpos, BH, ntq, c, qflip, smem, so);
 }
 
 // per head dimension: query blocks per wave, waves per workgroup, workgroups per CU
@@ -546,30 +639,36 @@ template <> struct Shape<256> { static constexpr int QB = 1, NW = 4, WPC = 2; };
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Nq, int Nk,
-                    int qpos, float c, uint32_t qflip, hipStream_t stream) {
+                    int qpos, float c, uint32_t qflip, SplitOut so, hipStream_t stream) {
     constexpr int QB = Shape<D>::QB, NW = Shape<D>::NW, WPC = Shape<D>::WPC;
     constexpr int BM = Tile<D, QB, NW, WPC>::BM;
     const int ntq = (Nq + BM - 1) / BM;
-    const long long nwg = (long long)BH * ntq;
+    const long long nwg = (long long)BH * ntq * (so.n > 0 ? so.n : 1);
     if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fa_fwd16_kernel<T, D, QB, NW, WPC, CAUSAL>), dim3((unsigned)nwg), dim3(64 * NW), 0, stream,
-                       (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, qpos, BH, ntq, c, qflip);
+    if (so.n > 0)
+        hipLaunchKernelGGL((fa_fwd16_kernel<T, D, QB, NW, WPC, CAUSAL, true>), dim3((unsigned)nwg), dim3(64 * NW), 0,
+                           stream, (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, qpos, BH, ntq, c, qflip,
+                           so);
+    else
+        hipLaunchKernelGGL((fa_fwd16_kernel<T, D, QB, NW, WPC, CAUSAL, false>), dim3((unsigned)nwg), dim3(64 * NW), 0,
+                           stream, (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, Nq, Nk, qpos, BH, ntq, c, qflip,
+                           so);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t dispatch16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Nq, int Nk,
-                      int qpos, int d, bool causal, float c, uint32_t qflip, hipStream_t stream) {
+                      int qpos, int d, bool causal, float c, uint32_t qflip, SplitOut so, hipStream_t stream) {
     switch (d) {
         case 64:
-            return causal ? launch16<T, 64, true>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, stream)
-                          : launch16<T, 64, false>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, stream);
+            return causal ? launch16<T, 64, true>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, so, stream)
+                          : launch16<T, 64, false>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, so, stream);
         case 128:
-            return causal ? launch16<T, 128, true>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, stream)
-                          : launch16<T, 128, false>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, stream);
+            return causal ? launch16<T, 128, true>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, so, stream)
+                          : launch16<T, 128, false>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, so, stream);
         case 256:
-            return causal ? launch16<T, 256, true>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, stream)
-                          : launch16<T, 256, false>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, stream);
+            return causal ? launch16<T, 256, true>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, so, stream)
+                          : launch16<T, 256, false>(q, k, v, o, lse, BH, Nq, Nk, qpos, c, qflip, so, stream);
         default:
             return hipErrorNotSupported;
     }
@@ -580,8 +679,21 @@ hipError_t dispatch16(const void* q, const void* k, const void* v, void* o, floa
 hipError_t launch_fwd_16(bool is_bf16, const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                          int Nq, int Nk, int qpos, int d, bool causal, float c, uint32_t qflip,
                          hipStream_t stream) {
-    return is_bf16 ? dispatch16<__bf16>(q, k, v, o, lse, BH, Nq, Nk, qpos, d, causal, c, qflip, stream)
-                   : dispatch16<_Float16>(q, k, v, o, lse, BH, Nq, Nk, qpos, d, causal, c, qflip, stream);
+    const SplitOut none{0, nullptr, nullptr};
+    return is_bf16 ? dispatch16<__bf16>(q, k, v, o, lse, BH, Nq, Nk, qpos, d, causal, c, qflip, none, stream)
+                   : dispatch16<_Float16>(q, k, v, o, lse, BH, Nq, Nk, qpos, d, causal, c, qflip, none, stream);
+}
+
+hipError_t launch_fwd_16_split(bool is_bf16, const void* q, const void* k, const void* v, void* o, float* lse,
+                               float* work, int nsplit, int BH, int Nq, int Nk, int qpos, int d, bool causal, float c,
+                               uint32_t qflip, hipStream_t stream) {
+    float* Op = work;
+    float* Lp = work + (size_t)BH * nsplit * Nq * d;
+    const SplitOut so{nsplit, Op, Lp};
+    hipError_t e = is_bf16 ? dispatch16<__bf16>(q, k, v, o, lse, BH, Nq, Nk, qpos, d, causal, c, qflip, so, stream)
+                           : dispatch16<_Float16>(q, k, v, o, lse, BH, Nq, Nk, qpos, d, causal, c, qflip, so, stream);
+    if (e != hipSuccess) return e;
+    return launch_merge_partials(is_bf16, Op, Lp, o, lse, BH, Nq, nsplit, d, stream);
 }
 
 }  // namespace fa

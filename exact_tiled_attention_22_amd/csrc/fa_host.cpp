@@ -229,6 +229,57 @@ int fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse
                     dtype == FA_BF16 ? "fa_fwd_rect(bf16)" : "fa_fwd_rect(f16)");
 }
 
+size_t fa_fwd_split_workspace_bytes(int B, int H, int Nq, int d, int nsplit) {
+    if (B <= 0 || H <= 0 || Nq <= 0 || d <= 0 || nsplit <= 0) return 0;
+    return static_cast<size_t>(B) * H * nsplit * Nq * (d + 1) * sizeof(float);
+}
+
+int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                 int q_start, int d, int causal, float scale, int dtype, int nsplit, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    const int eb = elem_bytes(dtype);
+    if (eb == 0) return fail(FA_ERR_DTYPE, "dtype code %d is not one of FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3", dtype);
+    if (dtype != FA_F16 && dtype != FA_BF16)
+        return fail(FA_ERR_UNSUPPORTED, "fa_fwd_split dtype %d (supported: FA_F16, FA_BF16)", dtype);
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+        return fail(FA_ERR_SHAPE, "negative size B=%d H=%d Nq=%d Nk=%d", B, H, Nq, Nk);
+    if (causal != 0 && causal != 1) return fail(FA_ERR_ARG, "causal must be 0 or 1, got %d", causal);
+    if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale must be finite");
+    if (causal ? (q_start < 0 || static_cast<long long>(q_start) + Nq > Nk) : q_start != 0)
+        return fail(FA_ERR_ARG, "q_start = %d: causal needs 0 <= q_start <= Nk - Nq (Nq=%d, Nk=%d), non-causal 0",
+                    q_start, Nq, Nk);
+    if (d != 64 && d != 128 && d != 256) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128, 256)", d);
+    if (nsplit < 1 || nsplit > 64) return fail(FA_ERR_ARG, "nsplit must be 1..64, got %d", nsplit);
+    const long long BH = static_cast<long long>(B) * H;
+    if (BH == 0 || Nq == 0) return FA_OK;
+    if (Nk == 0) return fail(FA_ERR_SHAPE, "Nq = %d queries against no keys", Nq);
+    if (int st = check_sizes(BH, Nq, d)) return st;
+    if (int st = check_sizes(BH, Nk, d)) return st;
+    if (int st = check_sizes(BH * nsplit, Nq, d + 1)) return st;
+    if (!q || !k || !v || !o || !workspace) return fail(FA_ERR_NULL, "q, k, v, o and workspace must be non-NULL");
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) || misaligned(workspace))
+        return fail(FA_ERR_ALIGN, "q, k, v, o, lse and workspace must be 16-byte aligned");
+    const size_t need = fa_fwd_split_workspace_bytes(B, H, Nq, d, nsplit);
+    if (workspace_bytes < need) return fail(FA_ERR_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    const size_t qbytes = static_cast<size_t>(BH) * Nq * d * eb, kbytes = static_cast<size_t>(BH) * Nk * d * eb;
+    if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kbytes) || overlaps(o, qbytes, v, kbytes))
+        return fail(FA_ERR_ARG, "o must not overlap q, k or v");
+    const size_t lbytes = static_cast<size_t>(BH) * Nq * 4;
+    if (overlaps(workspace, need, q, qbytes) || overlaps(workspace, need, k, kbytes) ||
+        overlaps(workspace, need, v, kbytes) || overlaps(workspace, need, o, qbytes) ||
+        (lse && overlaps(workspace, need, lse, lbytes)))
+        return fail(FA_ERR_ARG, "workspace must not overlap any tensor");
+    if (lse && overlaps(lse, lbytes, o, qbytes)) return fail(FA_ERR_ARG, "lse must not overlap o");
+    float c = static_cast<float>(std::fabs(static_cast<double>(scale)) * 1.4426950408889634);
+    if (!(c >= 1e-30f)) c = 1e-30f;
+    return from_hip(fa::launch_fwd_16_split(dtype == FA_BF16, q, k, v, o, lse, static_cast<float*>(workspace), nsplit,
+                                            static_cast<int>(BH), Nq, Nk, q_start, d, causal != 0, c,
+                                            std::signbit(scale) ? 0x80008000u : 0u,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                    dtype == FA_BF16 ? "fa_fwd_split(bf16)" : "fa_fwd_split(f16)");
+}
+
 size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
     if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
     return decode_bytes(static_cast<long long>(B) * H, Nq, Nk, d);

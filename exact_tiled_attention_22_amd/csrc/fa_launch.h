@@ -16,6 +16,19 @@ hipError_t launch_fwd_16(bool is_bf16, const void* q, const void* k, const void*
                          int BH, int Nq, int Nk, int qpos, int d, bool causal, float c, uint32_t qflip,
                          hipStream_t stream);
 
+// Same kernel with each query tile's key tiles split into nsplit contiguous shares (one workgroup per
+// share), followed by a merge launch: work = float32 [BH, nsplit, Nq, d] partial outputs, then
+// [BH, nsplit, Nq] partial lse (base 2).  For shapes with too few query tiles to fill the GPU.
+hipError_t launch_fwd_16_split(bool is_bf16, const void* q, const void* k, const void* v, void* o, float* lse,
+                               float* work, int nsplit, int BH, int Nq, int Nk, int qpos, int d, bool causal, float c,
+                               uint32_t qflip, hipStream_t stream);
+
+// Merge of per-share partial results: O = sum_s 2^(lse_s - lse) O_s, lse = log2 sum_s 2^lse_s (written in
+// natural-log units when lse != NULL).  Op [BH, nc, Nq, d], Lp [BH, nc, Nq]; an entry with lse_s = -inf
+// (a share without a visible key) contributes nothing.
+hipError_t launch_merge_partials(bool is_bf16, const float* Op, const float* Lp, void* o, float* lse, int BH, int Nq,
+                                 int nc, int d, hipStream_t stream);
+
 // float32 path: v_mfma_f32_32x32x2_f32.  c as above; qneg negates Q.
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           int BH, int N, int d, bool causal, float c, bool qneg, hipStream_t stream);

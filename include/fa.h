@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum {
     FA_F32 = 0,      /* float32 in, float32 out */
@@ -115,6 +115,27 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int H, int Nq, int Nk, int q_start, int d, int causal, float scale, int dtype,
                 void* stream);
+
+/*
+ * fa_fwd_rect with each query tile's key range split into `nsplit` contiguous shares handled by
+ * separate workgroups, each with its own online softmax (running maximum and sum over its share); a
+ * second launch merges the shares' partial results exactly: lse = log sum_s exp(lse_s) and
+ * O = sum_s exp(lse_s - lse) O_s (the same merge the decode path uses).  The result is the same
+ * attention (FlashAttention 2 + 3 concept card, "Kernpunkte": tiling and online softmax; the running
+ * maximum and correction factor of the glossary entry "Online-Softmax" are what makes partial results
+ * over key ranges mergeable).  For shapes whose B*H*ceil(Nq/128) workgroups cannot fill the GPU, e.g.
+ * one GPU's share of a sequence-sharded long-context forward.
+ *   Arguments as fa_fwd_rect, plus:
+ *   nsplit    : 1..64 shares per query tile (1 gives fa_fwd_rect's result bit for bit).
+ *   workspace : DEVICE scratch of at least fa_fwd_split_workspace_bytes(B, H, Nq, d, nsplit) bytes,
+ *               owned by the caller, 16-byte aligned, overlapping no tensor; contents on return are
+ *               unspecified.  Calls that share a workspace must not overlap in time.
+ * Returns an fa_status; nothing is enqueued on error.
+ */
+size_t fa_fwd_split_workspace_bytes(int B, int H, int Nq, int d, int nsplit);
+int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Nq, int Nk, int q_start, int d, int causal, float scale, int dtype,
+                 int nsplit, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Block absmax quantisation to OCP e4m3fn with an optional Hadamard rotation of the head dimension

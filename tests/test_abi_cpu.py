@@ -43,7 +43,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
-    assert set(names) == {"fa_fwd", "fa_fwd_ex", "fa_fwd_rect", "fa_bwd", "fa_fwd_decode", "fa_decode_workspace_bytes",
+    assert set(names) == {"fa_fwd", "fa_fwd_ex", "fa_fwd_rect", "fa_fwd_split", "fa_fwd_split_workspace_bytes",
+                          "fa_bwd", "fa_fwd_decode", "fa_decode_workspace_bytes",
                           "fa_fp8_prep", "fa_status_str", "fa_last_error", "fa_abi_version",
                           "fa_naive_row_stride", "fa_naive_workspace_bytes", "fa_naive_scores",
                           "fa_naive_softmax", "fa_naive_pv", "fa_fwd_naive"}
@@ -66,7 +67,7 @@ def test_validation_statuses(lib):
     lib.fa_last_error.restype = ctypes.c_char_p
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_abi_version.restype = ctypes.c_int
-    assert lib.fa_abi_version() == 2
+    assert lib.fa_abi_version() == 3
     big = 1 << 20  # fake, 16-aligned addresses: validation never dereferences them
     assert _fwd(lib, dtype=9) == FA_ERR_DTYPE
     assert _fwd(lib, N=-1) == FA_ERR_SHAPE
@@ -199,6 +200,43 @@ def test_rect_validation_statuses(lib):
     assert call(pp=[p[0], p[1], p[2], p[3], p[3]]) == FA_ERR_ARG  # lse aliases o
     assert call(Nq=0, pp=[None] * 5) == FA_OK
     assert call(B=0, pp=[None] * 5) == FA_OK
+
+
+def test_split_validation_statuses(lib):
+    f = lib.fa_fwd_split
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    f.argtypes = [vp] * 5 + [ci] * 7 + [ctypes.c_float, ci, ci, vp, ctypes.c_size_t, vp]
+    f.restype = ci
+    lib.fa_fwd_split_workspace_bytes.argtypes = [ci] * 5
+    lib.fa_fwd_split_workspace_bytes.restype = ctypes.c_size_t
+    wsb = lib.fa_fwd_split_workspace_bytes
+    assert wsb(2, 4, 100, 128, 3) == 2 * 4 * 3 * 100 * 129 * 4
+    assert wsb(0, 4, 100, 128, 3) == 0 and wsb(2, 4, 100, 128, 0) == 0
+    big = 1 << 26
+    p = [big * (i + 1) for i in range(6)]  # q k v o lse workspace
+    need = wsb(2, 4, 100, 128, 4)
+
+    def call(pp=None, B=2, H=4, Nq=100, Nk=300, q_start=0, d=128, causal=0, scale=0.1, dtype=2, ns=4, nb=need):
+        q, k, v, o, lse, ws = pp or p
+        return f(q, k, v, o, lse, B, H, Nq, Nk, q_start, d, causal, scale, dtype, ns, ws, nb, None)
+
+    # every call below fails validation (or is empty): nothing is launched on these fake pointers
+    assert call(dtype=0) == FA_ERR_UNSUPPORTED
+    assert call(dtype=9) == FA_ERR_DTYPE
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(Nq=-1) == FA_ERR_SHAPE
+    assert call(causal=2) == FA_ERR_ARG
+    assert call(scale=float("inf")) == FA_ERR_ARG
+    assert call(q_start=5) == FA_ERR_ARG
+    assert call(causal=1, q_start=201) == FA_ERR_ARG
+    assert call(ns=0) == FA_ERR_ARG and call(ns=65) == FA_ERR_ARG
+    assert call(nb=need - 1) == FA_ERR_ARG  # workspace too small
+    assert call(Nk=0) == FA_ERR_SHAPE
+    assert call(pp=[p[0], p[1], p[2], p[3], p[4], None]) == FA_ERR_NULL
+    assert call(pp=p[:5] + [p[5] + 8]) == FA_ERR_ALIGN
+    assert call(pp=p[:5] + [p[3]]) == FA_ERR_ARG  # workspace aliases o
+    assert call(pp=[p[0], p[1], p[2], p[0], p[4], p[5]]) == FA_ERR_ARG  # o aliases q
+    assert call(Nq=0, pp=[None] * 6) == FA_OK
 
 
 def test_naive_validation_statuses(lib):
