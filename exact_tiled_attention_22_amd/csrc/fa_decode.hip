@@ -335,23 +335,35 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(const T* __restrict__ Q
     DecodeVec<T, D>::run(Q, K, V, Op, Lp, Nk, nsplit, chunk, c, qflip);
 }
 
-// one workgroup of D threads per (b, h, query): thread t owns output column t
+// 256 threads per workgroup, D/4 per (b, h, query row): thread t owns output columns 4t .. 4t+3, read as
+// one float4 per partial; 1024/D rows per workgroup.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ Op, const float* __restrict__ Lp,
-                                                         T* __restrict__ O, float* __restrict__ LSE, int Nq, int nc) {
-    const int bh = blockIdx.x / Nq, query = blockIdx.x % Nq, col = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ Op, const float* __restrict__ Lp,
+                                                           T* __restrict__ O, float* __restrict__ LSE, int Nq, int nc,
+                                                           long long rows) {
+    constexpr int TPR = D / 4, RPB = 256 / TPR;
+    const long long r = (long long)blockIdx.x * RPB + threadIdx.x / TPR;  // (b, h, query) row
+    if (r >= rows) return;
+    const int col = (threadIdx.x % TPR) * 4;
+    const long long bh = r / Nq, query = r % Nq;
     const size_t base = (size_t)bh * nc * Nq + query;
     float M = -INFINITY;
     for (int i = 0; i < nc; ++i) M = fmaxf(M, Lp[base + (size_t)i * Nq]);
-    float L = 0.0f, acc = 0.0f;
+    float L = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int i = 0; i < nc; ++i) {
         const float lc = Lp[base + (size_t)i * Nq];
         const float w = lc == -INFINITY ? 0.0f : fast_exp2(lc - M);
         L += w;
-        acc = __builtin_fmaf(w, Op[(base + (size_t)i * Nq) * D + col], acc);
+        const f32x4 o = *(const f32x4*)(Op + (base + (size_t)i * Nq) * D + col);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, o[e], acc[e]);
     }
-    O[((size_t)bh * Nq + query) * D + col] = (T)(acc / L);
-    if (LSE != nullptr && col == 0) LSE[(size_t)bh * Nq + query] = (M + __log2f(L)) * 0.69314718055994531f;
+    typename Vec<T>::x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = (T)(acc[e] / L);
+    *(typename Vec<T>::x4*)(O + r * D + col) = out;
+    if (LSE != nullptr && col == 0) LSE[r] = (M + __log2f(L)) * 0.69314718055994531f;
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -373,8 +385,9 @@ hipError_t launch_decode_t(const void* q, const void* k, const void* v, void* o,
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)nm), dim3(D), 0, stream, (const float*)Op,
-                       (const float*)Lp, (T*)o, lse, Nq, nc);
+    constexpr int RPB = 1024 / D;
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)((nm + RPB - 1) / RPB)), dim3(256), 0, stream,
+                       (const float*)Op, (const float*)Lp, (T*)o, lse, Nq, nc, nm);
     return hipGetLastError();
 }
 
@@ -406,8 +419,9 @@ hipError_t launch_merge_partials(bool is_bf16, const float* Op, const float* Lp,
     auto go = [&](auto tag, auto dim) -> hipError_t {
         using T = decltype(tag);
         constexpr int D = decltype(dim)::value;
-        hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)nm), dim3(D), 0, stream, Op, Lp, (T*)o, lse, Nq,
-                           nc);
+        constexpr int RPB = 1024 / D;
+        hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)((nm + RPB - 1) / RPB)), dim3(256), 0, stream,
+                           Op, Lp, (T*)o, lse, Nq, nc, nm);
         return hipGetLastError();
     };
     switch (d) {
