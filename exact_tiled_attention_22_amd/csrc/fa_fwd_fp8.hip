@@ -240,7 +240,7 @@ struct Fwd8 {
             if (j + 1 < ntw) scores(smem + okn, qreg, nxt, krow0, h);
             // p~ = 2^(s*c_j - m + delta), rounded to e4m3, 4 per dword: keys h*32 + kb*16 + r
             i32x8 p;
-            float ls = 0.0f;
+            float part[8];  // row sum as a shallow tree: 4-term partial sums, then pairs
             const float add = delta - m_run;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -248,15 +248,14 @@ struct Fwd8 {
                 for (int w4 = 0; w4 < 4; ++w4) {
                     float e[4];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        e[t] = fast_exp2(__builtin_fmaf(cur[kb][w4 * 4 + t], cj, add));
-                        ls += e[t];
-                    }
+                    for (int t = 0; t < 4; ++t) e[t] = fast_exp2(__builtin_fmaf(cur[kb][w4 * 4 + t], cj, add));
+                    part[kb * 4 + w4] = (e[0] + e[1]) + (e[2] + e[3]);
                     int wd = 0;
                     wd = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], wd, false);
                     wd = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], wd, true);
                     p[kb * 4 + w4] = wd;
                 }
+            const float ls = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
             l_run += ls * lscale;
             // O^T += V8^T P~^T
             const char* vl = smem + ov;
