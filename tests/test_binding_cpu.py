@@ -17,6 +17,8 @@ def test_missing_library_raises(monkeypatch, tmp_path):
         fa.decode_workspace_bytes(1, 1, 1, 64, 128)
     with pytest.raises(RuntimeError, match="missing"):
         fa.naive_row_stride(100)
+    with pytest.raises(RuntimeError, match="missing"):
+        fa.split_workspace_bytes(1, 1, 8, 64, 2)
 
 
 @pytest.mark.parametrize("entry", ["fwd", "fwd_naive"])
@@ -30,6 +32,10 @@ def test_host_tensors_rejected_decode_and_bwd():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fwd_decode(q, q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.fwd_rect(q, q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.fwd_split(q, q, q, nsplit=2)
     lse = torch.zeros(1, 1, 8)
     with pytest.raises(ValueError):
         fa.bwd(q, q, q, q, lse, q)
