@@ -41,6 +41,8 @@ CASES = [
     ("f16", 256, 1, 1, 256, 4096, 3840, True, 8),
     ("bf16", 128, 2, 2, 500, 129, 0, False, 2),      # more queries than keys
     ("f16", 64, 1, 1, 333, 4000, 1234, True, 6),     # middle range of a sequence
+    ("bf16", 256, 1, 2, 300, 1000, 700, True, 3),    # d = 256 (in-order pipeline), ragged causal range
+    ("f16", 128, 1, 2, 1000, 1000, 0, True, 64),     # the largest share count: most shares empty for early rows
 ]
 
 
