@@ -16,7 +16,9 @@
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; the library allocates nothing
  *     and keeps no state between calls except a thread-local error string.
- *   - Tensors are contiguous row-major [B, H, N, d] (lse: [B, H, N], float32).  N_q = N_k = N.
+ *   - Tensors are contiguous row-major [B, H, N, d] (lse: [B, H, N], float32).  N_q = N_k = N for
+ *     fa_fwd, fa_fwd_ex and fa_bwd; fa_fwd_rect, fa_fwd_split and fa_fwd_decode take q as
+ *     [B, H, Nq, d] and k, v as [B, H, Nk, d].
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL = the null
  *     stream).  No call synchronises the host.  Calls are thread-safe.
  *   - Arguments are validated before anything is enqueued: a non-FA_OK return means no work was
