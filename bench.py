@@ -280,9 +280,9 @@ def bench_decode(args) -> int:
 def bench_shard(args, w) -> int:
     """One GPU's share of a sequence-sharded causal forward: with the query rows cut into G equal ranges
     (rank r owns rows [r*N/G, (r+1)*N/G)) and K/V gathered on every GPU, rank r attends its rows to the
-    keys they can see, [0, (r+1)*N/G).  A share has only B*H*N/(G*128) query tiles, too few workgroups
+    keys they can see, [0, (r+1)*N/G).  A share has only B*H*N/(G*BM) query tiles, too few workgroups
     to fill the GPU, so it runs through fa_fwd_split with each query tile's keys cut into enough shares
-    for about two workgroups per CU (fa_fwd_rect, unsplit, is timed beside it).  Every rank's share is
+    to fill every workgroup slot (fa_fwd_rect, unsplit, is timed beside it).  Every rank's share is
     timed on this one GPU (HIP events, median); the line reports the heaviest share (the last rank),
     which sets the step time of the sharded forward.  Flops per share follow the metric's convention:
     4*B*H*d*(Nq*q_start + Nq^2/2), which sums over the ranks to the workload's 4*B*H*N^2*d/2."""
@@ -301,8 +301,10 @@ def bench_shard(args, w) -> int:
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     q, k, v = (t.to(dev) for t in gen_qkv(w.B, w.H, w.N, w.d, w.dtype, w.cfg_id))
     nq = w.N // G
-    base_wg = w.B * w.H * ((nq + 127) // 128)
-    nsplit = max(1, min(64, -(-2 * cus // base_wg)))
+    # workgroups of the forward kernel: 128 query rows, two per CU (d <= 128); 256 rows, one per CU (d = 256)
+    bm, per_cu = (256, 1) if w.d >= 256 else (128, 2)
+    base_wg = w.B * w.H * ((nq + bm - 1) // bm)
+    nsplit = max(1, min(64, -(-per_cu * cus // base_wg)))
     ws = torch.empty(fa.split_workspace_bytes(w.B, w.H, nq, w.d, nsplit), dtype=torch.uint8, device=dev)
     shares = []
     for r in range(G):
