@@ -237,7 +237,18 @@ struct Fwd8 {
                     for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
                 }
             }
-            if (j + 1 < ntw) scores(smem + okn, qreg, nxt, krow0, h);
+            // d = 128: the next tile's scores are always computed (on a wave's last tile from a stage
+            // that holds some earlier tile: in bounds, result unused) so that they sit in one basic
+            // block with the exponentials and the value products, which the schedule below interleaves;
+            // the wave runs at raised priority meanwhile, as in the 16-bit kernel.  d = 256 has no
+            // registers to spare for that, and d = 64 (two score MFMAs per tile) measured slower with
+            // it; both keep the branch.
+            if constexpr (D == 128) {
+                __builtin_amdgcn_s_setprio(1);
+                scores(smem + okn, qreg, nxt, krow0, h);
+            } else if (j + 1 < ntw) {
+                scores(smem + okn, qreg, nxt, krow0, h);
+            }
             // p~ = 2^(s*c_j - m + delta), rounded to e4m3, 4 per dword: keys h*32 + kb*16 + r
             i32x8 p;
             float part[8];  // row sum as a shallow tree: 4-term partial sums, then pairs
@@ -272,6 +283,25 @@ struct Fwd8 {
                     vop[2 * u + 1] = t2[1];
                 }
                 oacc[cb] = mfma_fp8(vop, p, oacc[cb]);
+            }
+            if constexpr (D == 128) {
+                // each score MFMA followed by 8 vector instructions of the softmax (its K operands two
+                // ahead), then each value MFMA with the next V operand reads and 8 more
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int i = 0; i < 2 * KS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (i + 2 < 2 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int i = 0; i < CB; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (i + 1 < CB) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                }
+                __builtin_amdgcn_s_setprio(0);
             }
         };
         for (int j = 0; j < nt; j += 2) {
