@@ -173,6 +173,13 @@ struct Fwd8 {
             svmax = m > 0.0f ? m : 1.0f;
         }
         const float inv_svmax = 1.0f / svmax;
+        // this tile's K and V block scales, loaded one tile ahead (scalar loads, so that no tile waits
+        // on the scalar cache)
+        float sk_j = 1.0f, sv_j = 1.0f;
+        if (SQ != nullptr) {
+            sk_j = SK[srow];
+            sv_j = SV[srow];
+        }
 
         i32x8 qreg[KS];
         {
@@ -197,10 +204,13 @@ struct Fwd8 {
             const int kv0 = j * BN;
             float cj = c * sq, delta = kBoost8, lscale = 1.0f / 64.0f;
             if (SQ != nullptr) {
-                cj *= SK[srow + j];
-                const float rv = SV[srow + j] * inv_svmax;  // sv[j] / svmax in (0, 1]
+                cj *= sk_j;
+                const float rv = sv_j * inv_svmax;  // sv[j] / svmax in (0, 1]
                 delta += __log2f(rv);
                 lscale *= __builtin_amdgcn_rcpf(rv);  // hardware reciprocal (1 ulp): a row-sum factor
+                const int jn = min(j + 1, nblk - 1);
+                sk_j = SK[srow + jn];
+                sv_j = SV[srow + jn];
             }
             // mask
             if ((kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > q0w)) {
