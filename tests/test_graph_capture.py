@@ -1,5 +1,5 @@
 """The library's launches under HIP graph capture (torch.cuda.CUDAGraph): the entry points allocate
-nothing and issue only kernels on the caller's stream, so a captured forward, backward or decode replays
+nothing and issue only kernels on the caller's stream, so a captured forward, backward, decode or split forward replays
 to the same bits as the eager call.  Each graph is replayed several times with eager work and
 synchronisation in between, and every replay is compared with the eager result."""
 
@@ -89,3 +89,32 @@ def test_decode_replay_bitwise():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1]), f"decode replay {rep} differs"
+
+
+def test_split_replay_bitwise():
+    # key shares and their merge (two launches, partials in the caller's workspace); the workspace is
+    # overwritten between replays: every share writes all of its partial rows, empty ones included
+    fa = _fa()
+    dev = torch.device("cuda")
+    B, H, Nq, Nk, d, ns = 1, 3, 300, 2000, 128, 5
+    q = gen_qkv(B, H, Nq, d, "bf16", seed=44)[0].to(dev)
+    _, k, v = (t.to(dev) for t in gen_qkv(B, H, Nk, d, "bf16", seed=45))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.split_workspace_bytes(B, H, Nq, d, ns), dtype=torch.uint8, device=dev)
+
+    def step():
+        fa.fwd_split(q, k, v, nsplit=ns, causal=True, q_start=Nk - Nq, out=o, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (o.clone(), lse.clone())
+    graph = _capture(step)
+    for rep in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ws.fill_(255)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1]), f"split replay {rep} differs"
