@@ -358,6 +358,21 @@ struct BwdKV {
                         if (cb & 1) __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            if constexpr (D <= 128) {
+                // S^T / dP^T MFMAs paced by their operand reads, then dV / dK MFMAs by theirs
+                __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+                for (int i = 0; i < KS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    if (i + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int i = 0; i < 4 * CB; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (i + 2 < 4 * CB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+            }
         };
         for (int tq = t0; tq < ntq; tq += 2) {
             iteration(tq, VBYTES, VBYTES + STAGE);
