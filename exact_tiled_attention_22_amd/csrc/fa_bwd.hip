@@ -210,6 +210,21 @@ struct BwdQ {
                         if (cb & 1) __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            if constexpr (D <= 128) {
+                // S^T / dP^T MFMAs two at a time behind their operand reads, then dQ MFMAs behind theirs
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int i = 0; i < 2 * KS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    if (i + 2 < 2 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int i = 0; i < 4 * CB; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (i + 2 < 4 * CB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+            }
         };
         for (int j = 0; j < nt; j += 2) {
             iteration(j, 0, TILE, 2 * TILE, 3 * TILE);
