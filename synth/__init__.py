@@ -9,6 +9,7 @@ from .gen import (  # noqa: F401
     Workload,
     gen_fp8_workload,
     gen_qkv,
+    gen_qkv_device,
     gen_signs,
     normal_f32,
     workload,

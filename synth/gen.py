@@ -110,6 +110,25 @@ def gen_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int,
     return tuple(out)
 
 
+def gen_qkv_device(B: int, H: int, N: int, d: int, dtype: str, seed: int, device, count: int = 3):
+    """``count`` tensors [B, H, N, d] drawn directly in device memory, for shapes too large to draw
+    on the host in reasonable time (billions of elements).
+
+    Recipe: tensor t comes from torch's generator of that device seeded with ``seed * 16 + t``,
+    i.i.d. standard normal in float32, rounded to the storage dtype.  Repeatable for a given device
+    type and torch build; the oracle's side copies the generated (rounded) values it needs back to
+    the host, so both sides still see the same bits.
+    """
+    tdt = _TORCH_DTYPES[dtype]
+    out = []
+    for t in range(count):
+        g = torch.Generator(device=device).manual_seed(int(seed) * 16 + t)
+        x = torch.randn((B, H, N, d), generator=g, device=device, dtype=torch.float32)
+        out.append(x.to(tdt))
+        del x
+    return tuple(out)
+
+
 def gen_signs(d: int, seed: int) -> np.ndarray:
     """Random +/-1 vector (int8, length d) for the head-dimension rotation."""
     bits = _rng(seed, 4).integers(0, 2, size=d, dtype=np.int8)

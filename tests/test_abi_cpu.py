@@ -83,6 +83,8 @@ def test_validation_statuses(lib):
     assert _fwd(lib, q=big, k=big * 2, v=big * 3, o=big * 4, lse=big * 5 + 4) == FA_ERR_ALIGN
     assert _fwd(lib, q=big, k=big * 2, v=big * 3, o=big) == FA_ERR_ARG  # o aliases q
     assert _fwd(lib, B=1 << 16, H=1 << 16, q=big, k=big * 2, v=big * 3, o=big * 4) == FA_ERR_SHAPE
+    far = 1 << 40  # disjoint fake regions for the longest sequences
+    assert _fwd(lib, N=1 << 21, q=far, k=far * 2, v=far * 3, o=far * 4, lse=far * 5) == FA_ERR_SHAPE
     for s in range(8):
         assert lib.fa_status_str(s)
     assert lib.fa_status_str(99) == b"unknown fa_status"
