@@ -87,6 +87,14 @@ struct Geo {
     }
 };
 
+// A value the optimiser cannot see through.  The non-causal d = 256 kernels pass their per-wave tile
+// bound through it so that the tile step's early exit stays a branch: without it the step becomes
+// one scheduling region and 79 (dQ) / 200 (dK/dV) registers spill.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
 // ---------------------------------------------------------------------------------------------
 // D = rowsum(dO o O) in float32: D/8 lanes per row, 16-byte loads, a butterfly sum over the row's lanes.
 template <typename T, int D>
@@ -134,7 +142,7 @@ struct BwdQ {
         const size_t head = (size_t)bh * N * D;
         const int q0 = qt * BM, q0w = q0 + wave * QW, query = q0w + n32, qrow = min(query, N - 1);
         const int nt = ((CAUSAL ? min(N, q0 + BM) : N) + BN - 1) / BN;
-        const int ntw = ((CAUSAL ? min(N, q0w + QW) : N) + BN - 1) / BN;
+        const int ntw = CAUSAL ? (min(N, q0w + QW) + BN - 1) / BN : (D >= 256 ? opaque(nt) : nt);
         const Geo<CPR> g(lane);
 
         // B operands of S^T = K Q^T and dP^T = V dO^T: this lane's query row, 8 columns per k-step
@@ -282,7 +290,7 @@ struct BwdKV {
         const int k0 = kt * BK, kw0 = k0 + wave * KW, key = kw0 + n32, krow = min(key, N - 1);
         const int ntq = (N + BQ - 1) / BQ;
         const int t0 = CAUSAL ? k0 / BQ : 0;        // first query tile with a visible key of the workgroup
-        const int t0w = CAUSAL ? kw0 / BQ : 0;      // ... of this wave
+        const int t0w = CAUSAL ? kw0 / BQ : (D >= 256 ? opaque(0) : 0);  // ... of this wave
         const Geo<CPR> g(lane);
         const int vrow = wave * KW + n32;           // this lane's V row in LDS
 

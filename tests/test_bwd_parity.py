@@ -95,12 +95,13 @@ def test_bwd_full_size_sampled_heads(causal):
         _check([g[b, h] for g in got], ref, f"B16H16N1024 head {b},{h} causal={causal}")
 
 
-def test_bwd_d256_long_sampled_heads():
-    # d = 256 at a longer sequence (fp16 causal, the large-head forward workload's dtype and mask)
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_d256_long_sampled_heads(causal):
+    # d = 256 at a longer sequence (fp16, the large-head forward workload's dtype; both masks)
     B, H, N, d = 1, 2, 4096, 256
     q, k, v, do = _inputs(B, H, N, d, "f16", seed=31)
     scale = float(np.float32(1 / np.sqrt(d)))
-    got = _gpu_bwd(q, k, v, do, True, scale)
+    got = _gpu_bwd(q, k, v, do, causal, scale)
     for h in range(H):
-        ref = attention_bwd_rows(q[0, h], k[0, h], v[0, h], do[0, h], True, scale)
-        _check([g[0, h] for g in got], ref, f"f16 d256 N{N} head {h} causal=True")
+        ref = attention_bwd_rows(q[0, h], k[0, h], v[0, h], do[0, h], causal, scale)
+        _check([g[0, h] for g in got], ref, f"f16 d256 N{N} head {h} causal={causal}")
