@@ -3,16 +3,18 @@
 
 One step = one full forward pass (work partition, Q/K/V tiles, scores, mask, online softmax, P*V,
 epilogue; for the fp8 workload also the three preparation launches) over one batch of seeded
-synthetic inputs already resident in HBM.  Default workload: bf16 B16 H16 N1024 d128 non-causal.
+synthetic inputs already resident in HBM.  Default workload: fp16 B1 H8 N16384 d256 causal (the
+largest one-GPU workload).
 With --bwd a step is one backward pass (delta, dQ, dK/dV launches) from the forward's saved o and
 lse, counted as 10*B*H*N^2*d flops (/2 causal).  --decode times the decode path (K/V cache read
 GB/s); --naive times the unfused path (scores, softmax, P*V through HBM) beside the fused kernel.
 
 Prints ONE JSON line (rank 0):
   metric/value/unit         attention fwd TFLOP/s = 4*B*H*N^2*d (/2 causal) / time per step
-  roofline                  dominant kernel: algorithmic flops per launch / average launch time
-                            (HIP event pairs around each launch on the launch stream, in a pass
-                            after the timed one), against the MI355X dense peak
+  roofline                  dominant kernel: algorithmic flops per launch / its GPU time per launch
+                            over the timed region (HIP events on the launch stream), against the
+                            MI355X dense peak; "settled" adds the same launches after the timed
+                            region once the clock has settled (context, not the value)
   cpu_baseline              the float64 CPU oracle timed on a bounded sample of the same workload
 """
 
@@ -104,31 +106,67 @@ def ingest_counters(cfg_id: int, fetch_csv: str, write_csv: str) -> int:
 def time_steps(step, steps: int, dev) -> float:
     """Wall-clock ms per step over exactly `steps` back-to-back steps, synchronised on both sides (the
     launches are enqueued without anything between them, as a caller would issue them)."""
+    return timed_region(step, steps, dev)[0]
+
+
+def timed_region(step, steps: int, dev, inner=None):
+    """The timed region: exactly `steps` back-to-back steps, synchronised on both sides.  Returns
+    (wall-clock ms per step, GPU ms per step).  The GPU time comes from HIP events recorded on the launch
+    stream (torch's current stream, on which the binding launches) right before the first and right after
+    the last step, so it covers the same launches as the wall clock and cannot exceed it.  With `inner`
+    (a pair of callables (pre, kernel) making up one step), an event pair brackets each kernel() call
+    inside the region instead, and the GPU time is the average of those pairs: the dominant kernel's own
+    launch duration when a step holds several launches."""
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+    if inner is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(steps):
+            step()
+        b.record(stream)
+        torch.cuda.synchronize(dev)
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        return wall, a.elapsed_time(b) / steps
+    pre, kernel = inner
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for a, b in ev:
+        pre()
+        a.record(stream)
+        kernel()
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
+def settled_stats(step, dev, min_ms: float = 300.0, min_steps: int = 20, pre=None) -> dict:
+    """Per-step event durations after the timed region, once the clock has settled: steps run back to
+    back for at least `min_ms` first, then event pairs around each of at least `min_steps` further steps
+    (and at least `min_ms` of them).  Context beside the timed region, never the reported value."""
     import torch
 
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize(dev)
-    return (time.perf_counter() - t0) * 1e3 / steps
-
-
-def launch_ms(step, steps: int, dev) -> float:
-    """Average duration of one step from a HIP event pair recorded around each step on the launch stream
-    (torch's current stream, which the binding launches on); a pass of its own, after the timed one,
-    because the markers between launches keep consecutive kernels from overlapping."""
-    import torch
-
-    stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize(dev)
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize(dev)
-    return sum(a.elapsed_time(b) for a, b in ev) / steps
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(8):
+            if pre is not None:
+                pre()
+            step()
+        torch.cuda.synchronize(dev)
+    t = []
+    t0 = time.perf_counter()
+    while len(t) < min_steps or (time.perf_counter() - t0) * 1e3 < min_ms:
+        st = launch_stats(step, min_steps, dev, pre=pre)
+        t.extend(st["all"])
+    t.sort()
+    return {"steps": len(t), "median_ms": round(t[len(t) // 2], 5), "min_ms": round(t[0], 5),
+            "avg_ms": round(sum(t) / len(t), 5)}
 
 
 def launch_stats(step, steps: int, dev, pre=None) -> dict:
@@ -147,7 +185,7 @@ def launch_stats(step, steps: int, dev, pre=None) -> dict:
         b.record(stream)
     torch.cuda.synchronize(dev)
     t = sorted(a.elapsed_time(b) for a, b in ev)
-    return {"avg": sum(t) / len(t), "median": t[len(t) // 2], "min": t[0]}
+    return {"avg": sum(t) / len(t), "median": t[len(t) // 2], "min": t[0], "all": t}
 
 
 def cold_launch_ms(step, reps: int, dev, flush_bytes: int = 512 << 20, pre=None) -> float:
@@ -254,8 +292,7 @@ def bench_decode(args) -> int:
 
     for _ in range(args.warmup):
         step()
-    ms_per_step = time_steps(step, args.steps, dev)
-    avg_ms = launch_ms(step, args.steps, dev)
+    ms_per_step, avg_ms = timed_region(step, args.steps, dev)
     nbytes = 2.0 * c["B"] * c["H"] * c["Nk"] * c["d"] * 2
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
@@ -269,7 +306,8 @@ def bench_decode(args) -> int:
                      "kernel": ("decode_vec_kernel" if c["Nq"] == 1 else "decode_split_kernel")
                      + " + decode_merge_kernel (the launches of one fa_fwd_decode call)",
                      "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
-                     "frac": round(achieved / 8000.0, 4), "traffic": None, "kernel_avg_ms": round(avg_ms, 5)},
+                     "frac": round(achieved / 8000.0, 4), "traffic": None, "kernel_avg_ms": round(avg_ms, 5),
+                     "timing": "HIP events on the launch stream over the timed region (first to last launch, / steps)"},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = decode_cpu_baseline(c)
@@ -472,7 +510,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=500)
     # the GPU needs ~40 ms of sustained load to reach its working clock: warm up well past that
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
+    ap.add_argument("--config", type=int, default=4,
+                    help="workload id 1..5 (default 4: fp16 B1 H8 N16384 d256 causal, the largest one-GPU workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", action="store_true",
                     help="time the decode path (1 query against a 32768-key cache, B8 H32 d128 bf16)")
@@ -561,16 +600,18 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
-    # timed region: exactly K back-to-back steps; then the per-launch duration from event pairs
-    ms_per_step = time_steps(step, args.steps, dev)
-    if w.dtype == "fp8" and not args.bwd:
-        # the dominant kernel is the e4m3 forward: the preparation launches sit outside its event pair
-        ls = launch_stats(fwd8, args.steps, dev, pre=prep)
+    # timed region: exactly K back-to-back steps, wall clock and HIP events on the launch stream.  The
+    # e4m3 step holds three preparation launches and the forward kernel: event pairs bracket each
+    # forward launch inside the region, so the roofline covers that kernel alone.
+    fp8_fwd = w.dtype == "fp8" and not args.bwd
+    ms_per_step, avg_launch_ms = timed_region(step, args.steps, dev, inner=(prep, fwd8) if fp8_fwd else None)
+    # context, after the timed region: the same launches once the clock has settled, and cold caches
+    if fp8_fwd:
+        settled = settled_stats(fwd8, dev, pre=prep)
         cold_ms = cold_launch_ms(fwd8, 20, dev, pre=prep)
     else:
-        ls = launch_stats(step, args.steps, dev)
+        settled = settled_stats(step, dev)
         cold_ms = cold_launch_ms(step, 20, dev)
-    avg_launch_ms = ls["avg"]
 
     flops = w.flops * (2.5 if args.bwd else 1.0)  # backward: dS, dQ, dK, dV and the recomputed S = 10 N^2 d
     kernel = ("fa_bwd (delta, dQ and dK/dV launches of one call)" if args.bwd else
@@ -604,9 +645,13 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
+            # GPU time per launch over the timed region (HIP events on the launch stream)
             "kernel_avg_ms": round(avg_launch_ms, 5),
-            "kernel_median_ms": round(ls["median"], 5),
-            "kernel_min_ms": round(ls["min"], 5),
+            "timing": "HIP events on the launch stream over the timed region" + (
+                " (one pair around each forward launch)" if fp8_fwd else " (first to last launch, / steps)"),
+            # context only: after the timed region, with the clock settled; and with cold caches
+            "settled": dict(settled, tflops=round(flops / (settled["median_ms"] * 1e-3) / 1e12, 2),
+                            frac=round(flops / (settled["median_ms"] * 1e-3) / 1e12 / peak, 4)),
             "cold_kernel_ms": round(cold_ms, 5),
         },
     }

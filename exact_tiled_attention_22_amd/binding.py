@@ -166,14 +166,25 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, 
     if return_lse:
         lse = _out(lse, (B, H, N), torch.float32, q.device, "lse")
     s8 = None
-    keep = []
-    if code == FA_FP8_E4M3 and fp8_scales is not None:
-        sq, sk, sv = (t.contiguous() for t in fp8_scales)
-        keep = [sq, sk, sv]
+    if fp8_scales is not None:
+        if code != FA_FP8_E4M3:
+            raise ValueError(f"fp8_scales apply to float8_e4m3fn inputs only, got {q.dtype}")
+        if int(block) <= 0:
+            raise ValueError(f"block must be positive, got {block}")
+        if len(fp8_scales) != 3:
+            raise ValueError("fp8_scales must be a triple (sq, sk, sv)")
+        # the C ABI reads B*H*ceil(N/block) floats from each pointer: the tensors must hold exactly that
+        shape = (B, H, -(-N // int(block)))
+        for name, t in zip(("sq", "sk", "sv"), fp8_scales):
+            if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device != q.device
+                    or tuple(t.shape) != shape or not t.is_contiguous()):
+                desc = f"{t.dtype} {tuple(t.shape)} on {t.device}" if isinstance(t, torch.Tensor) else type(t).__name__
+                raise ValueError(f"fp8 scale {name} must be a contiguous float32 tensor of shape {shape} on "
+                                 f"{q.device}, got {desc}")
+        sq, sk, sv = fp8_scales
         s8 = ctypes.pointer(_Fp8Scales(sq.data_ptr(), sk.data_ptr(), sv.data_ptr(), int(block)))
     st = lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse if return_lse else None),
                          B, H, N, d, int(bool(causal)), float(scale), code, s8, _stream(q.device))
-    del keep
     _check(st, "fa_fwd_ex")
     return out, (lse if return_lse else None)
 
@@ -337,8 +348,9 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = No
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
             raise ValueError("o and dout must match q in shape, dtype and device, contiguous")
     B, H, N, d = q.shape
-    if lse is None or lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if (lse is None or lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise ValueError(f"lse must be a contiguous float32 [B, H, N] tensor on {q.device}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = _out(dq, q.shape, q.dtype, q.device, "dq")
@@ -350,6 +362,16 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = No
                       _stream(q.device))
     _check(st, "fa_bwd")
     return dq, dk, dv
+
+
+def _sign_buffer(signs, d: int):
+    """The rotation signs as the host int8 array fa_fp8_prep reads: exactly d values, each +1 or -1."""
+    sign_list = [int(s) for s in (signs.tolist() if hasattr(signs, "tolist") else signs)]
+    if len(sign_list) != d:
+        raise ValueError(f"signs must hold d = {d} values, got {len(sign_list)}")
+    if any(s not in (1, -1) for s in sign_list):
+        raise ValueError("signs must be +1 or -1")
+    return (ctypes.c_int8 * d)(*sign_list)
 
 
 def fp8_prep(x, signs=None, block: int = 64, out=None, scales=None):
@@ -367,10 +389,7 @@ def fp8_prep(x, signs=None, block: int = 64, out=None, scales=None):
     nblk = -(-N // block) if block > 0 else 0
     out = _out(out, x.shape, torch.float8_e4m3fn, x.device, "out")
     scales = _out(scales, tuple(x.shape[:-2]) + (max(nblk, 0),), torch.float32, x.device, "scales")
-    sign_buf = None
-    if signs is not None:
-        sign_list = [int(s) for s in (signs.tolist() if hasattr(signs, "tolist") else signs)]
-        sign_buf = (ctypes.c_int8 * len(sign_list))(*sign_list)
+    sign_buf = None if signs is None else _sign_buffer(signs, d)
     st = lib().fa_fp8_prep(_ptr(x), DTYPE_CODE[x.dtype], _ptr(out), _ptr(scales),
                            ctypes.cast(sign_buf, ctypes.c_void_p) if sign_buf is not None else None,
                            int(block), int(BH), int(N), int(d), _stream(x.device))
