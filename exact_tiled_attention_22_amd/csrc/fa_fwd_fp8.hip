@@ -11,13 +11,15 @@
 //   * scores: s_ij = (q8_i . k8_j) * sq[i/64] * sk[j/64] * scale.  A wave's 32 query rows share one
 //     Q block and a 64-key tile is one K block, so the per-tile softmax constant
 //     c_j = |scale| log2(e) sq sk[j] absorbs both scales: p = 2^(s8 * c_j - m);
-//   * values: O_i = sum_j p_ij sv[j/64] v8_j / l_i.  With svmax the largest V scale of the head, the
-//     kernel rounds  p~ = p * 2^6 * sv[j] / svmax = 2^(s8 * c_j - m + 6 + log2(sv[j]/svmax))  to e4m3
-//     (the extra terms join the subtraction, so they cost nothing per element), accumulates p~ . v8 on
-//     the MFMA, keeps the row sum of the unscaled p (l += sum(p~) * 2^-6 * svmax / sv[j], once per
-//     tile), and the epilogue multiplies by svmax / (2^6 l).  The running maximum is corrected as soon
-//     as it grows by more than 2^2, so p <= 4 and p~ <= 256 stays inside e4m3's range (448); the 2^6
-//     lifts most probabilities out of e4m3's subnormal range (below 2^-6).
+//   * values: O_i = sum_j p_ij sv[j/64] v8_j / l_i.  The kernel rounds p~ = p * 2^6 to e4m3 (an exact
+//     power-of-two boost that lifts most probabilities out of e4m3's subnormal range, below 2^-6; the
+//     largest probability of a row, 1 when the running maximum was just set, stays exact), multiplies
+//     each 64-key tile's values on the MFMA with a zero accumulator, T = v8^T p~^T, and adds T * sv[j]
+//     to the float32 output accumulator.  The V block scale thus never enters the rounded operand:
+//     folding it into p~ made the dominant probability of a row a non-power-of-two that e4m3 rounds
+//     by up to 2^-4.  The row sum keeps the unrounded p (l += sum(p~) * 2^-6) and the epilogue divides
+//     by 2^6 l.  The running maximum is corrected as soon as it grows by more than 2^2, so p <= 4 and
+//     p~ <= 256 stays inside e4m3's range (448).  A zero V scale makes its block contribute nothing.
 //
 // Layouts as in the 16-bit kernel (S^T = K Q^T, O^T += V^T P^T), adapted to 64-wide k-steps: the K
 // rows feeding the score MFMA are permuted so that wave half h holds the scores of keys h*32 + 0..31
@@ -162,17 +164,8 @@ struct Fwd8 {
         }
         lds_barrier();
 
-        // scales: this wave's Q block, the largest V scale of the head
-        float sq = 1.0f, svmax = 1.0f;
-        if (SQ != nullptr) {
-            sq = SQ[srow + min(q0w, N - 1) / 64];
-            float m = 0.0f;
-            for (int t = lane; t < nblk; t += 64) m = fmaxf(m, SV[srow + t]);
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-            svmax = m > 0.0f ? m : 1.0f;
-        }
-        const float inv_svmax = 1.0f / svmax;
+        // this wave's Q block scale
+        const float sq = SQ != nullptr ? SQ[srow + min(q0w, N - 1) / 64] : 1.0f;
         // this tile's K and V block scales, loaded one tile ahead (scalar loads, so that no tile waits
         // on the scalar cache)
         float sk_j = 1.0f, sv_j = 1.0f;
@@ -190,6 +183,14 @@ struct Fwd8 {
         f32x16 oacc[CB];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16{};
+        // d = 128: a tile's values T (and its V scale) wait in registers until the next iteration adds
+        // them to the accumulator, so that the matrix latency is covered (e4m3 B4 H16 N4096: 345 -> 326 us;
+        // d = 64 measured slower with it, d = 256 has no registers for it)
+        constexpr bool DEFER = D == 128;
+        f32x16 tv[DEFER ? CB : 1];
+        float wpend = 0.0f;
+#pragma unroll
+        for (int cb = 0; cb < (DEFER ? CB : 1); ++cb) tv[cb] = f32x16{};
         float m_run = -INFINITY, l_run = 0.0f;
 
         f32x16 s0[2], s1[2];
@@ -202,12 +203,10 @@ struct Fwd8 {
             if (j + 1 < nt) copy_rows<LPT>(Vh, (j + 1) * BN, N, lbase + dv, tid, wave);
             if (j >= ntw) return;
             const int kv0 = j * BN;
-            float cj = c * sq, delta = kBoost8, lscale = 1.0f / 64.0f;
+            float cj = c * sq;
+            const float wv = sv_j;  // this tile's V block scale
             if (SQ != nullptr) {
                 cj *= sk_j;
-                const float rv = sv_j * inv_svmax;  // sv[j] / svmax in (0, 1]
-                delta += __log2f(rv);
-                lscale *= __builtin_amdgcn_rcpf(rv);  // hardware reciprocal (1 ulp): a row-sum factor
                 const int jn = min(j + 1, nblk - 1);
                 sk_j = SK[srow + jn];
                 sv_j = SV[srow + jn];
@@ -222,6 +221,12 @@ struct Fwd8 {
                         const int key = kv0 + h * 32 + kb * 16 + r;
                         if (key >= N || (CAUSAL && key > query)) cur[kb][r] = -INFINITY;
                     }
+            }
+            if constexpr (DEFER) {
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[cb][r] = __builtin_fmaf(tv[cb][r], wpend, oacc[cb][r]);
             }
             // running maximum with lazy correction
             {
@@ -259,10 +264,10 @@ struct Fwd8 {
             } else if (j + 1 < ntw) {
                 scores(smem + okn, qreg, nxt, krow0, h);
             }
-            // p~ = 2^(s*c_j - m + delta), rounded to e4m3, 4 per dword: keys h*32 + kb*16 + r
+            // p~ = 2^(s*c_j - m + 6), rounded to e4m3, 4 per dword: keys h*32 + kb*16 + r
             i32x8 p;
             float part[8];  // row sum as a shallow tree: 4-term partial sums, then pairs
-            const float add = delta - m_run;
+            const float add = kBoost8 - m_run;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -277,7 +282,7 @@ struct Fwd8 {
                     p[kb * 4 + w4] = wd;
                 }
             const float ls = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
-            l_run += ls * lscale;
+            l_run += ls * (1.0f / 64.0f);
             // O^T += V8^T P~^T
             const char* vl = smem + ov;
 #pragma unroll
@@ -292,8 +297,16 @@ struct Fwd8 {
                     vop[2 * u] = t2[0];
                     vop[2 * u + 1] = t2[1];
                 }
-                oacc[cb] = mfma_fp8(vop, p, oacc[cb]);
+                // this tile's values alone, then scaled by its V block scale into the accumulator
+                if constexpr (DEFER) {
+                    tv[cb] = mfma_fp8(vop, p, f32x16{});
+                } else {
+                    const f32x16 t = mfma_fp8(vop, p, f32x16{});
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[cb][r] = __builtin_fmaf(t[r], wv, oacc[cb][r]);
+                }
             }
+            wpend = wv;
             if constexpr (D == 128) {
                 // each score MFMA followed by 8 vector instructions of the softmax (its K operands two
                 // ahead), then each value MFMA with the next V operand reads and 8 more
@@ -319,12 +332,18 @@ struct Fwd8 {
             if (j + 1 < nt) iteration(j + 1, s1, s0, TL::OFF_K0, TL::OFF_V1, TL::OFF_K1, TL::OFF_V0);
         }
 
+        if constexpr (DEFER) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[cb][r] = __builtin_fmaf(tv[cb][r], wpend, oacc[cb][r]);
+        }
         // the output leaves through this wave's LDS region as whole rows (every stage is free once
         // all waves are past their last tile)
         lds_barrier();
         char* wl = smem + wave * QW * D * 2;
         const float lt = halves_sum(l_run);
-        const float inv = svmax / (64.0f * lt);  // undo the 2^kBoost8 carried by p~
+        const float inv = 1.0f / (64.0f * lt);  // undo the 2^kBoost8 carried by p~
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll

@@ -89,8 +89,12 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * "Drei technische Hebel", item 3 "FP8-Blockquantisierung": blockwise 8-bit operands).
  * Identical to fa_fwd for other dtypes (s8 is then ignored).  For FA_FP8_E4M3 the inputs are e4m3
  * codes; the value of element [b,h,n,:] is code * scale[b*H+h][n / block].  s8 == NULL means all
- * scales are 1.  Scores and the P*V product accumulate in float32; P is rounded to e4m3 for the
- * second product; o is bfloat16.
+ * scales are 1.  Scores and the P*V product accumulate in float32; P (times an exact 2^6) is rounded
+ * to e4m3 for the second product, whose 64-key blocks are each multiplied by their V scale in float32;
+ * o is bfloat16.  Scales are read on the device, so they are not validated: they must be finite and
+ * non-negative, as fa_fp8_prep writes them (a V scale of 0 makes its block contribute nothing; other
+ * values give unspecified output, never a fault).  The three arrays must each hold
+ * B*H*ceil(N/block) floats.
  */
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int N, int d, int causal, float scale, int dtype,

@@ -1,10 +1,10 @@
 """GPU parity of the attention backward (fa_bwd, through the C ABI) against the float64 oracle.
 
 Tolerance (derived, not printed on the pages): the kernels round P and dS to the 16-bit operand type
-(relative error <= 2^-9 for bfloat16, 2^-12 for float16) and read o in that type, and accumulate in
+(unit roundoff u = 2^-8 for bfloat16, 2^-11 for float16), read o in that type, and accumulate in
 float32; each gradient is a sum of such rounded products, so its error relative to the gradient's
-own scale stays near the operand rounding.  The bar is max|d - d_ref| <= 2e-2 * max|d_ref| for every
-gradient, bfloat16 and float16 alike.
+own scale stays at a few u.  The bar is max|d - d_ref| <= 5 u * max|d_ref| per dtype: 1.95e-2 for
+bfloat16 and 2.44e-3 for float16.
 """
 
 import numpy as np
@@ -16,7 +16,7 @@ from synth import gen_qkv
 
 pytestmark = pytest.mark.gpu
 
-REL = 2e-2
+REL = {"bf16": 5 * 2.0 ** -8, "f16": 5 * 2.0 ** -11}
 
 
 def _fa():
@@ -41,7 +41,8 @@ def _gpu_bwd(q, k, v, do, causal, scale):
     return [t.float().cpu().numpy() for t in (dq, dk, dv)]
 
 
-def _check(got, ref, label):
+def _check(got, ref, label, dtype):
+    bar = REL[dtype]
     worst = 0.0
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
         assert np.isfinite(g).all(), f"{label} {name} not finite"
@@ -50,7 +51,7 @@ def _check(got, ref, label):
         rel = err / max(scale, 1e-30)
         worst = max(worst, rel)
         print(f"{label} {name}: max|err| {err:.3e}  max|ref| {scale:.3e}  ratio {rel:.3e}", flush=True)
-        assert err <= REL * scale + 1e-6, f"{label} {name}: {err} > {REL} * {scale}"
+        assert err <= bar * scale + 1e-6, f"{label} {name}: {err} > {bar} * {scale}"
     return worst
 
 
@@ -68,7 +69,7 @@ def test_bwd_sweep(dtype, d, N, causal):
     scale = float(np.float32(1 / np.sqrt(d)))
     got = _gpu_bwd(q, k, v, do, causal, scale)
     ref = attention_bwd_ref(q, k, v, do, causal, scale)
-    _check(got, ref, f"{dtype} d{d} N{N} causal={causal}")
+    _check(got, ref, f"{dtype} d{d} N{N} causal={causal}", dtype)
 
 
 def test_bwd_negative_scale_and_determinism():
@@ -78,7 +79,7 @@ def test_bwd_negative_scale_and_determinism():
     b = _gpu_bwd(q, k, v, do, False, scale)
     for x, y in zip(a, b):
         assert np.array_equal(x, y), "backward is not bitwise repeatable"
-    _check(a, attention_bwd_ref(q, k, v, do, False, scale), "negative scale")
+    _check(a, attention_bwd_ref(q, k, v, do, False, scale), "negative scale", "bf16")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -92,7 +93,7 @@ def test_bwd_full_size_sampled_heads(causal):
     for bh in rng.choice(B * H, size=4, replace=False):
         b, h = divmod(int(bh), H)
         ref = attention_bwd_rows(q[b, h], k[b, h], v[b, h], do[b, h], causal, scale)
-        _check([g[b, h] for g in got], ref, f"B16H16N1024 head {b},{h} causal={causal}")
+        _check([g[b, h] for g in got], ref, f"B16H16N1024 head {b},{h} causal={causal}", "bf16")
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -104,4 +105,4 @@ def test_bwd_d256_long_sampled_heads(causal):
     got = _gpu_bwd(q, k, v, do, causal, scale)
     for h in range(H):
         ref = attention_bwd_rows(q[0, h], k[0, h], v[0, h], do[0, h], causal, scale)
-        _check([g[0, h] for g in got], ref, f"f16 d256 N{N} head {h} causal={causal}")
+        _check([g[0, h] for g in got], ref, f"f16 d256 N{N} head {h} causal={causal}", "f16")

@@ -113,6 +113,43 @@ def test_fp8_forward_unit_scales_and_negative_scale():
         assert r <= 3e-2 and float(np.abs(lse.cpu().numpy() - lse_ref).max()) <= 1e-3
 
 
+@pytest.mark.parametrize("B,H,N,d,causal", [(2, 4, 300, 128, False), (2, 4, 300, 128, True), (4, 4, 200, 64, True),
+                                             (2, 8, 260, 256, False), (1, 8, 130, 256, True), (4, 4, 257, 128, False)])
+def test_fp8_xcd_partition_element_wise(B, H, N, d, causal):
+    # B*H a multiple of 8 (the work partition's XCD branch), every element against oracle (i)
+    r_i, _, dl = _fp8_case(B, H, N, d, causal, seed=B * 100 + H * 10 + N + d)
+    assert r_i <= 3e-2 and dl <= 1e-3
+    assert r_i <= 8e-3  # the kernel's own error budget
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fp8_zero_v_scale_block(d):
+    """A V block whose scale is 0 dequantises to zeros: its keys keep their softmax weight but add no value
+    (scales of exactly 0 are never written by the preparation, which gives an all-zero block scale 1)."""
+    fa = _fa()
+    N = 200
+    q, k, v = gen_qkv(1, 2, N, d, "bf16", seed=40 + d)
+    signs = gen_signs(d, seed=d)
+    dev = torch.device("cuda")
+    q8, sq = fa.fp8_prep(q.to(dev), signs, 64)
+    k8, sk = fa.fp8_prep(k.to(dev), signs, 64)
+    v8, sv = fa.fp8_prep(v.to(dev), None, 64)
+    sv[0, 1, 1] = 0.0  # second 64-key block of head 1
+    scale = float(np.float32(1 / np.sqrt(d)))
+    o, lse = fa.fwd(q8, k8, v8, causal=False, scale=scale, fp8_scales=(sq, sk, sv))
+    torch.cuda.synchronize()
+    cq, csq = fp8_prep_ref(q, signs, 64)
+    ck, csk = fp8_prep_ref(k, signs, 64)
+    cv, csv = fp8_prep_ref(v, None, 64)
+    csv[0, 1, 1] = 0.0
+    o_i, lse_i = fp8_attention_ref(cq, csq, ck, csk, cv, csv, 64, False, scale)
+    o = o.float().cpu().numpy()
+    r = _rmse(o, o_i)
+    dl = float(np.abs(lse.cpu().numpy() - lse_i).max())
+    print(f"fp8 zero V scale d{d}: RMSE {r:.3e}, max|dlse| {dl:.2e}", flush=True)
+    assert np.isfinite(o).all() and r <= 3e-2 and dl <= 1e-3
+
+
 def test_fp8_full_config5_sampled_rows():
     fa = _fa()
     w = CONFIGS[5]
@@ -127,13 +164,15 @@ def test_fp8_full_config5_sampled_rows():
     lse = lse.cpu().numpy()
     rng = np.random.default_rng(55)
     err_i, err_ii, worst_l = [], [], 0.0
-    for bh in rng.choice(w.B * w.H, size=3, replace=False):
-        b, h = divmod(int(bh), w.H)
+    dense = set(int(x) for x in rng.choice(w.B * w.H, size=3, replace=False))
+    for bh in range(w.B * w.H):
+        # every head: 62 random rows on three of them, 6 on the others (the first and last row included)
+        b, h = divmod(bh, w.H)
         cq, csq = fp8_prep_ref(q[b, h][None], signs, 64)
         ck, csk = fp8_prep_ref(k[b, h][None], signs, 64)
         cv, csv = fp8_prep_ref(v[b, h][None], None, 64)
         qd, kd, vd = (dequantize_blocks(c, s_, 64)[0] for c, s_ in ((cq, csq), (ck, csk), (cv, csv)))
-        rows = np.unique(np.concatenate([[0, w.N - 1], rng.integers(0, w.N, 62)]))
+        rows = np.unique(np.concatenate([[0, w.N - 1], rng.integers(0, w.N, 62 if bh in dense else 4)]))
         o_i, lse_i = attention_rows(qd, kd, vd, rows, w.causal, w.scale)
         o_ii, _ = attention_rows(q[b, h], k[b, h], v[b, h], rows, w.causal, w.scale)
         err_i.append(o[b, h][rows] - o_i)
@@ -145,3 +184,7 @@ def test_fp8_full_config5_sampled_rows():
           f"max|dlse| {worst_l:.2e}", flush=True)
     assert np.isfinite(o).all()
     assert r_i <= 3e-2 and worst_l <= 1e-3
+    # the kernel's own error budget on this workload (a regression check beside the 3e-2 contract): a CPU
+    # model of the kernel's rounding (exact power-of-two boost of p, V block scale applied in float32,
+    # lazy maximum with slack 2^2, bf16 output) gives 4.0e-3 against the dequantised-input oracle
+    assert r_i <= 8e-3, f"e4m3 kernel error {r_i:.3e} above its 8e-3 budget"

@@ -8,7 +8,7 @@
 
 Inputs are drawn on the device (synth.gen_qkv_device); the sampled heads are copied back to the host
 for the oracle.  Tolerances are those of the other parity tests: max|dO| <= 1e-2, max|dlse| <= 1e-3,
-and max|d - d_ref| <= 2e-2 max|d_ref| per gradient.
+and max|d - d_ref| <= 5 * 2^-8 max|d_ref| per gradient (bfloat16).
 """
 
 import math
@@ -22,7 +22,7 @@ from synth import gen_qkv_device
 
 pytestmark = pytest.mark.gpu
 
-TOL_O, TOL_LSE, REL = 1e-2, 1e-3, 2e-2
+TOL_O, TOL_LSE, REL = 1e-2, 1e-3, 5 * 2.0 ** -8  # the backward parity bar for bfloat16 (5 unit roundoffs)
 N_MAX = (1 << 21) - 1
 
 

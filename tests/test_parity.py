@@ -78,21 +78,49 @@ def test_config1_tiny_fp32_full():
 
 @pytest.mark.parametrize("cfg_id", [2, 3, 4])
 def test_full_size_configs_sampled_rows(cfg_id):
+    # every head: its first and last row and one random row in each 128-row query tile, so every
+    # workgroup of the launch (128 or 256 query rows of one head) has checked rows; four heads add 29
     w = CONFIGS[cfg_id]
     q, k, v = gen_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=w.cfg_id)
     o, lse = _run(q, k, v, w.causal, w.scale)
     rng = np.random.default_rng(100 + cfg_id)
     worst_o = worst_l = 0.0
-    heads = rng.choice(w.B * w.H, size=min(4, w.B * w.H), replace=False)
-    for bh in heads:
-        b, h = divmod(int(bh), w.H)
-        rows = np.unique(np.concatenate([[0, 1, w.N - 1], rng.integers(0, w.N, 29)]))
+    dense = set(int(x) for x in rng.choice(w.B * w.H, size=min(4, w.B * w.H), replace=False))
+    checked = 0
+    for bh in range(w.B * w.H):
+        b, h = divmod(bh, w.H)
+        starts = np.arange(0, w.N, 128)
+        rows = [0, w.N - 1] + list(starts + rng.integers(0, 128, starts.size))
+        if bh in dense:
+            rows += list(rng.integers(0, w.N, 29))
+        rows = np.unique(np.clip(np.array(rows), 0, w.N - 1))
         o_ref, lse_ref = attention_rows(q[b, h], k[b, h], v[b, h], rows, w.causal, w.scale)
         worst_o = max(worst_o, float(np.abs(o[b, h][rows] - o_ref).max()))
         worst_l = max(worst_l, float(np.abs(lse[b, h][rows] - lse_ref).max()))
-    print(f"{w.name}: sampled max|dO|={worst_o:.3e} max|dlse|={worst_l:.3e}", flush=True)
+        checked += rows.size
+    print(f"{w.name}: {checked} rows over all {w.B * w.H} heads, max|dO|={worst_o:.3e} max|dlse|={worst_l:.3e}",
+          flush=True)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     assert worst_o <= TOL_O and worst_l <= TOL_LSE
+
+
+# B*H a multiple of 8: the work partition hands whole heads to each XCD (its remapped branch); several
+# query tiles per head, ragged N, both masks, every element compared
+XCD = [
+    ("bf16", 128, 2, 4, 300, False), ("bf16", 128, 2, 4, 300, True), ("f16", 128, 4, 4, 257, True),
+    ("f16", 128, 4, 4, 257, False), ("bf16", 64, 4, 4, 200, True), ("f16", 64, 2, 4, 390, False),
+    ("bf16", 256, 1, 8, 520, True), ("f16", 256, 2, 8, 300, False), ("f16", 256, 2, 4, 260, True),
+    ("bf16", 256, 4, 4, 130, False),
+]
+
+
+@pytest.mark.parametrize("dtype,d,B,H,N,causal", XCD)
+def test_xcd_partition_element_wise(dtype, d, B, H, N, causal):
+    q, k, v = gen_qkv(B, H, N, d, dtype, seed=B * 1000 + H * 100 + N + d)
+    scale = _f32(1 / math.sqrt(d))
+    o, lse = _run(q, k, v, causal, scale)
+    o_ref, lse_ref = attention_ref(q, k, v, causal, scale)
+    _compare(o, lse, o_ref, lse_ref, f"{dtype} d{d} B{B} H{H} N{N} causal={causal}")
 
 
 # long sequences: 64-bit head offsets, thousands of key tiles per query tile, the longest causal skip
