@@ -13,10 +13,12 @@ from .binding import (  # noqa: F401
     FaError,
     abi_version,
     bwd,
+    DECODE_NOALLOC_BYTES,
     decode_workspace_bytes,
     fp8_prep,
     fwd,
     fwd_decode,
+    fwd_decode_noalloc,
     fwd_naive,
     fwd_rect,
     fwd_split,

@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_split_workspace_bytes.restype = ctypes.c_size_t
     L.fa_fwd_decode.argtypes = [vp] * 5 + [i] * 6 + [f, i, vp, ctypes.c_size_t, vp]
     L.fa_fwd_decode.restype = i
+    L.fa_fwd_decode_noalloc.argtypes = [vp] * 5 + [i] * 6 + [f, i, vp]
+    L.fa_fwd_decode_noalloc.restype = i
     L.fa_decode_workspace_bytes.argtypes = [i] * 5
     L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.fa_naive_row_stride.argtypes = [i]
@@ -268,6 +270,30 @@ def fwd_decode(q, k, v, *, causal: bool = False, scale: float | None = None, out
     st = lib().fa_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, int(bool(causal)),
                              float(scale), DTYPE_CODE[q.dtype], _ptr(workspace), workspace.numel(), _stream(q.device))
     _check(st, "fa_fwd_decode")
+    return out, lse
+
+
+DECODE_NOALLOC_BYTES = 64 << 20  # FA_DECODE_NOALLOC_BYTES: the library-held decode workspace per GPU
+
+
+def fwd_decode_noalloc(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """fwd_decode without a workspace, through fa_fwd_decode_noalloc: the partial results go to the
+    library's own device array (64 MiB per GPU), so the call allocates nothing when ``out`` and ``lse`` are
+    given.  Calls overlapping in time on one GPU race on that array.  Returns (o, lse)."""
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("q, k, v must be contiguous 4-D GPU tensors")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must be [B, H, Nk, d] of q's dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = _out(out, q.shape, q.dtype, q.device, "out")
+    lse = _out(lse, (B, H, Nq), torch.float32, q.device, "lse")
+    st = lib().fa_fwd_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d,
+                                     int(bool(causal)), float(scale), DTYPE_CODE[q.dtype], _stream(q.device))
+    _check(st, "fa_fwd_decode_noalloc")
     return out, lse
 
 

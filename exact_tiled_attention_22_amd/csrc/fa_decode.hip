@@ -12,6 +12,7 @@
 //      which is the same softmax over the union of the chunks.
 // The waves share nothing, so there is no workgroup barrier; each waits only for its own copies.
 // Causal: query i (of Nq) sees keys j <= i + Nk - Nq (the queries are the last Nq positions).
+#include <mutex>
 #include <type_traits>
 
 #include "fa_common.h"
@@ -430,6 +431,34 @@ hipError_t launch_merge_partials(bool is_bf16, const float* Op, const float* Lp,
         case 256: return is_bf16 ? go(__bf16{}, std::integral_constant<int, 256>{}) : go(_Float16{}, std::integral_constant<int, 256>{});
         default: return hipErrorNotSupported;
     }
+}
+
+// ---- library-held workspace of the decode path, for callers that cannot allocate ----
+// One array per GPU (the code object's device variable), kept until the process ends; it holds the
+// partial results of the last fa_fwd_decode_noalloc call on that GPU.  Every call overwrites each entry
+// it reads (an empty key chunk stores O_c = 0, lse_c = -inf), so nothing needs clearing between calls;
+// calls that overlap in time on one GPU race on it.  Host code never passes the array's name to a
+// kernel: that is a host-side stand-in, not a device address.  decode_scratch_ptr returns the address
+// that hipGetSymbolAddress gives for the current device, looked up once per device.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch_ptr(float** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = static_cast<float*>(p);
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_decode_16(bool is_bf16, const void* q, const void* k, const void* v, void* o, float* lse, float* work,

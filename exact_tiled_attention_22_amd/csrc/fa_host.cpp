@@ -285,43 +285,92 @@ size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
     return decode_bytes(static_cast<long long>(B) * H, Nq, Nk, d);
 }
 
-int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
-                  int d, int causal, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-    g_err[0] = '\0';
+}  // extern "C"
+
+namespace {
+
+static_assert(fa::kDecodeScratchBytes == FA_DECODE_NOALLOC_BYTES, "the header states the library-held size");
+
+// Checks shared by the decode entry points; own_ws: the library-held array replaces the caller workspace.
+int decode_check(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                 int d, int causal, float scale, int dtype, const void* ws, size_t ws_bytes, bool own_ws,
+                 const char* fn) {
     if (dtype != FA_F16 && dtype != FA_BF16) {
         if (elem_bytes(dtype) == 0) return fail(FA_ERR_DTYPE, "dtype code %d is not a fa_dtype", dtype);
-        return fail(FA_ERR_UNSUPPORTED, "fa_fwd_decode dtype %d (supported: FA_F16, FA_BF16)", dtype);
+        return fail(FA_ERR_UNSUPPORTED, "%s dtype %d (supported: FA_F16, FA_BF16)", fn, dtype);
     }
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return fail(FA_ERR_SHAPE, "negative size B=%d H=%d Nq=%d Nk=%d", B, H, Nq, Nk);
     if (causal != 0 && causal != 1) return fail(FA_ERR_ARG, "causal must be 0 or 1, got %d", causal);
     if (!std::isfinite(scale)) return fail(FA_ERR_ARG, "scale must be finite");
     if (d != 64 && d != 128 && d != 256)
-        return fail(FA_ERR_UNSUPPORTED, "fa_fwd_decode head dimension d=%d (supported: 64, 128, 256)", d);
-    if (Nq > 32) return fail(FA_ERR_UNSUPPORTED, "fa_fwd_decode takes at most 32 queries per head, got %d", Nq);
+        return fail(FA_ERR_UNSUPPORTED, "%s head dimension d=%d (supported: 64, 128, 256)", fn, d);
+    if (Nq > 32) return fail(FA_ERR_UNSUPPORTED, "%s takes at most 32 queries per head, got %d", fn, Nq);
     if (Nq > Nk) return fail(FA_ERR_SHAPE, "fewer keys (%d) than queries (%d)", Nk, Nq);
     const long long BH = static_cast<long long>(B) * H;
     if (BH == 0 || Nq == 0) return FA_OK;
     if (int st = check_sizes(BH, Nk, d)) return st;
-    if (!q || !k || !v || !o || !workspace) return fail(FA_ERR_NULL, "q, k, v, o and workspace must be non-NULL");
-    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) || misaligned(workspace))
+    if (!q || !k || !v || !o || (!own_ws && !ws))
+        return fail(FA_ERR_NULL, own_ws ? "q, k, v and o must be non-NULL" : "q, k, v, o and workspace must be non-NULL");
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) || misaligned(ws))
         return fail(FA_ERR_ALIGN, "q, k, v, o, lse and workspace must be 16-byte aligned");
     const size_t need = decode_bytes(BH, Nq, Nk, d);
-    if (workspace_bytes < need) return fail(FA_ERR_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (own_ws) {
+        if (need > fa::kDecodeScratchBytes)
+            return fail(FA_ERR_UNSUPPORTED, "%s: this shape needs %zu bytes of workspace, more than the library-held "
+                        "%zu bytes (use fa_fwd_decode with a caller workspace)", fn, need, fa::kDecodeScratchBytes);
+    } else if (ws_bytes < need) {
+        return fail(FA_ERR_ARG, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+    }
     const size_t qb = static_cast<size_t>(BH) * Nq * d * 2, kb = static_cast<size_t>(BH) * Nk * d * 2;
     if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb))
         return fail(FA_ERR_ARG, "o must not overlap q, k or v");
-    if (overlaps(workspace, need, q, qb) || overlaps(workspace, need, k, kb) || overlaps(workspace, need, v, kb) ||
-        overlaps(workspace, need, o, qb) || (lse && overlaps(workspace, need, lse, static_cast<size_t>(BH) * Nq * 4)))
+    if (!own_ws && (overlaps(ws, need, q, qb) || overlaps(ws, need, k, kb) || overlaps(ws, need, v, kb) ||
+                    overlaps(ws, need, o, qb) || (lse && overlaps(ws, need, lse, static_cast<size_t>(BH) * Nq * 4))))
         return fail(FA_ERR_ARG, "workspace must not overlap any tensor");
     if (lse && overlaps(lse, static_cast<size_t>(BH) * Nq * 4, o, qb)) return fail(FA_ERR_ARG, "lse must not overlap o");
+    return FA_OK;
+}
+
+int decode_launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                  int d, int causal, float scale, int dtype, float* work, void* stream) {
+    const long long BH = static_cast<long long>(B) * H;
     float c = static_cast<float>(std::fabs(static_cast<double>(scale)) * 1.4426950408889634);
     if (!(c >= 1e-30f)) c = 1e-30f;
     int nw = 4, ns = 1, ck = 32;
     decode_plan(BH, Nq, Nk, d, &nw, &ns, &ck);
-    return from_hip(fa::launch_decode_16(dtype == FA_BF16, q, k, v, o, lse, static_cast<float*>(workspace),
-                                         static_cast<int>(BH), Nq, Nk, d, causal != 0, ns, ck, c,
-                                         std::signbit(scale) ? 0x80008000u : 0u, reinterpret_cast<hipStream_t>(stream)),
+    return from_hip(fa::launch_decode_16(dtype == FA_BF16, q, k, v, o, lse, work, static_cast<int>(BH), Nq, Nk, d,
+                                         causal != 0, ns, ck, c, std::signbit(scale) ? 0x80008000u : 0u,
+                                         reinterpret_cast<hipStream_t>(stream)),
                     dtype == FA_BF16 ? "fa_fwd_decode(bf16)" : "fa_fwd_decode(f16)");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                  int d, int causal, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    if (int st = decode_check(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, workspace, workspace_bytes, false,
+                              "fa_fwd_decode"))
+        return st;
+    if (static_cast<long long>(B) * H == 0 || Nq == 0) return FA_OK;
+    return decode_launch(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, static_cast<float*>(workspace), stream);
+}
+
+int fa_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                          int Nk, int d, int causal, float scale, int dtype, void* stream) {
+    g_err[0] = '\0';
+    if (int st = decode_check(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, nullptr, 0, true,
+                              "fa_fwd_decode_noalloc"))
+        return st;
+    if (static_cast<long long>(B) * H == 0 || Nq == 0) return FA_OK;
+    float* work = nullptr;
+    const hipError_t e = fa::decode_scratch_ptr(&work);
+    if (e != hipSuccess)
+        return fail(FA_ERR_HIP, "fa_fwd_decode_noalloc: device address of the library-held workspace: %s",
+                    hipGetErrorString(e));
+    return decode_launch(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, work, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,

@@ -56,6 +56,11 @@ hipError_t launch_decode_16(bool is_bf16, const void* q, const void* k, const vo
                             int BH, int Nq, int Nk, int d, bool causal, int nsplit, int chunk, float c, uint32_t qflip,
                             hipStream_t stream);
 
+// Library-held decode workspace (fa_fwd_decode_noalloc): its size, and its device address on the current
+// device (looked up once per device with hipGetSymbolAddress).
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+hipError_t decode_scratch_ptr(float** ptr);
+
 // unfused attention (bf16 / fp16, d in {64, 128, 256}): S = scale Q K^T as float32 [BH, N, ld]; P = softmax(S)
 // in the input dtype [BH, N, ld] (zero on the padding columns) with lse; O = P V.  ld = N rounded up to 64.
 hipError_t launch_naive_scores_16(bool is_bf16, const void* q, const void* k, float* s, int BH, int N, int d, int ld,

@@ -15,7 +15,8 @@
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; the library allocates nothing
- *     and keeps no state between calls except a thread-local error string.
+ *     and keeps no state between calls except a thread-local error string (and, for
+ *     fa_fwd_decode_noalloc only, one device array per GPU).
  *   - Tensors are contiguous row-major [B, H, N, d] (lse: [B, H, N], float32).  N_q = N_k = N for
  *     fa_fwd, fa_fwd_ex and fa_bwd; fa_fwd_rect, fa_fwd_split and fa_fwd_decode take q as
  *     [B, H, Nq, d] and k, v as [B, H, Nk, d].
@@ -183,6 +184,21 @@ size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
 int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int Nq, int Nk, int d, int causal, float scale, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_decode without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The partial
+ * results go to a library-held array of FA_DECODE_NOALLOC_BYTES bytes per GPU (a device variable of
+ * the library, kept until the process ends); the call allocates nothing.  Shapes whose
+ * fa_decode_workspace_bytes(B, H, Nq, Nk, d) exceeds FA_DECODE_NOALLOC_BYTES return
+ * FA_ERR_UNSUPPORTED before anything is enqueued (use fa_fwd_decode with a caller workspace).  Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on the same GPU (other streams,
+ * other threads) race and give undefined results; calls ordered on one stream are safe.  Arguments,
+ * result and errors are otherwise those of fa_fwd_decode; the output is bitwise the same.
+ */
+#define FA_DECODE_NOALLOC_BYTES (64u << 20)
+int fa_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int Nq, int Nk, int d, int causal, float scale, int dtype, void* stream);
 
 /*
  * Attention backward: the gradients of fa_fwd's output with respect to q, k and v for a given output

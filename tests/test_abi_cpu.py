@@ -44,7 +44,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_ex", "fa_fwd_rect", "fa_fwd_split", "fa_fwd_split_workspace_bytes",
-                          "fa_bwd", "fa_fwd_decode", "fa_decode_workspace_bytes",
+                          "fa_bwd", "fa_fwd_decode", "fa_decode_workspace_bytes", "fa_fwd_decode_noalloc",
                           "fa_fp8_prep", "fa_status_str", "fa_last_error", "fa_abi_version",
                           "fa_naive_row_stride", "fa_naive_workspace_bytes", "fa_naive_scores",
                           "fa_naive_softmax", "fa_naive_pv", "fa_fwd_naive"}
@@ -169,6 +169,41 @@ def test_decode_validation_statuses(lib):
     assert call(work=p[1]) == FA_ERR_ARG  # workspace overlaps k
     assert call(pp=[p[0], p[1], p[2], p[0], p[4]]) == FA_ERR_ARG  # o aliases q
     assert call(Nq=0) == FA_OK
+
+
+def test_decode_noalloc_validation_statuses(lib):
+    f = lib.fa_fwd_decode_noalloc
+    vp = ctypes.c_void_p
+    f.argtypes = [vp] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.c_int, vp]
+    f.restype = ctypes.c_int
+    ws = lib.fa_decode_workspace_bytes
+    ws.argtypes = [ctypes.c_int] * 5
+    ws.restype = ctypes.c_size_t
+    limit = 64 << 20  # FA_DECODE_NOALLOC_BYTES
+    big = 1 << 36
+    p = [big * (i + 1) for i in range(5)]  # q k v o lse (fake, never touched)
+
+    def call(pp=None, B=2, H=4, Nq=1, Nk=1000, d=128, causal=0, scale=0.1, dtype=2):
+        return f(*(pp or p), B, H, Nq, Nk, d, causal, scale, dtype, None)
+
+    # every call below fails validation (or is empty): nothing is launched, no device is touched
+    assert call(dtype=0) == FA_ERR_UNSUPPORTED
+    assert call(dtype=7) == FA_ERR_DTYPE
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(Nq=33) == FA_ERR_UNSUPPORTED
+    assert call(Nq=5, Nk=4) == FA_ERR_SHAPE
+    assert call(causal=2) == FA_ERR_ARG
+    assert call(scale=float("nan")) == FA_ERR_ARG
+    assert call(pp=[p[0], p[1], None, p[3], p[4]]) == FA_ERR_NULL
+    assert call(pp=[p[0] + 4, p[1], p[2], p[3], p[4]]) == FA_ERR_ALIGN
+    assert call(pp=[p[0], p[1], p[2], p[0], p[4]]) == FA_ERR_ARG  # o aliases q
+    assert call(Nq=0) == FA_OK and call(B=0) == FA_OK
+    # a shape whose workspace exceeds the library-held array is refused with a clear message
+    B, H, Nq, Nk, d = 64, 64, 32, 4096, 256
+    assert ws(B, H, Nq, Nk, d) > limit
+    assert f(*p, B, H, Nq, Nk, d, 0, 0.1, 2, None) == FA_ERR_UNSUPPORTED
+    lib.fa_last_error.restype = ctypes.c_char_p
+    assert b"library-held" in lib.fa_last_error()
 
 
 def test_rect_validation_statuses(lib):
