@@ -25,45 +25,11 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// 16-byte-chunk XOR swizzle of an LDS row (the forward pass's, for the same two access patterns:
-// a 16-row operand fetch of one chunk and a transposing fetch of 4 chunks x 4 rows).
-template <int CPR>
-__device__ __forceinline__ int bswz(int row) {
-    if constexpr (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
-    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
-
-// Copy rows [r0, r0 + ROWS) of a [N, D] slice (2-byte elements) into an LDS tile with THREADS
-// threads; rows past N repeat row N-1 (they are masked).  Slot s holds chunk (s % CPR) ^ swz(row).
-template <typename T, int D, int ROWS, int THREADS>
-__device__ __forceinline__ void copy_tile(const T* __restrict__ src, int r0, int N, uint32_t lds, int tid,
-                                          int wave) {
-    constexpr int CPR = D / 8, NL = ROWS * CPR / THREADS;
-    static_assert(ROWS * CPR % THREADS == 0, "tile splits evenly");
-    if (r0 + ROWS <= N) {
-        const T* base = src + (size_t)r0 * D;
-#pragma unroll
-        for (int t = 0; t < NL; ++t) {
-            const int slot = t * THREADS + tid;
-            const int row = slot / CPR;
-            const int c = (slot % CPR) ^ bswz<CPR>(row);
-            dma16s(base, (uint32_t)((row * D + c * 8) * (int)sizeof(T)),
-                   lds + (uint32_t)((t * THREADS + wave * 64) * 16));
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < NL; ++t) {
-            const int slot = t * THREADS + tid;
-            const int row = slot / CPR;
-            const int c = (slot % CPR) ^ bswz<CPR>(row);
-            dma16(src + (size_t)min(r0 + row, N - 1) * D + c * 8, lds + (uint32_t)((t * THREADS + wave * 64) * 16));
-        }
-    }
-}
-
-// Per-lane fetch geometry inside an LDS tile of 64 rows (lane = 32 h + n32).
+// Per-lane fetch geometry inside an LDS tile (row-major rows, XOR chunk swizzle: XorRows in
+// fa_common.h), lane = 32 h + n32.
 template <int CPR>
 struct Geo {
+    using L = XorRows<CPR>;
     int prow, h;        // A operand: permuted row prow (+32 for the second block), chunk 2*ks + h
     int trow, tcc, tb;  // transposing read: row u*4 + trow, chunk cb*4 + tcc, byte tb
     __device__ __forceinline__ Geo(int lane) {
@@ -76,14 +42,10 @@ struct Geo {
         tb = (i16 & 1) * 8;
     }
     // A operand for k-step ks of row block rb
-    __device__ __forceinline__ int aoff(int rb, int ks) const {
-        const int row = rb * 32 + prow;
-        return (row * CPR + ((2 * ks + h) ^ bswz<CPR>(row))) * 16;
-    }
+    __device__ __forceinline__ int aoff(int rb, int ks) const { return L::slot(rb * 32 + prow, 2 * ks + h) * 16; }
     // transposed operand (rows = d block cb, contraction = 16 tile rows from 16 * st), half u
     __device__ __forceinline__ int toff(int cb, int st, int u) const {
-        const int row = st * 16 + u * 4 + trow;
-        return (row * CPR + ((cb * 4 + tcc) ^ bswz<CPR>(row))) * 16 + tb;
+        return L::slot(st * 16 + u * 4 + trow, cb * 4 + tcc) * 16 + tb;
     }
 };
 
@@ -154,8 +116,8 @@ struct BwdQ {
         }
         const float lse2 = LSE[(size_t)bh * N + qrow] * kLog2e;
         const float dd = Dl[(size_t)bh * N + qrow];
-        copy_tile<T, D, BN, THREADS>(K + head, 0, N, lbase, tid, wave);
-        copy_tile<T, D, BN, THREADS>(V + head, 0, N, lbase + TILE, tid, wave);
+        copy_tile<XorRows<CPR>, BN, CPR, THREADS>(K + head, 0, N, D * 2, lbase, tid, wave);
+        copy_tile<XorRows<CPR>, BN, CPR, THREADS>(V + head, 0, N, D * 2, lbase + TILE, tid, wave);
 
         f32x16 acc[CB];
 #pragma unroll
@@ -165,8 +127,8 @@ struct BwdQ {
             wait_vmcnt<0>();
             lds_barrier();
             if (j + 1 < nt) {
-                copy_tile<T, D, BN, THREADS>(K + head, (j + 1) * BN, N, lbase + dk, tid, wave);
-                copy_tile<T, D, BN, THREADS>(V + head, (j + 1) * BN, N, lbase + dv, tid, wave);
+                copy_tile<XorRows<CPR>, BN, CPR, THREADS>(K + head, (j + 1) * BN, N, D * 2, lbase + dk, tid, wave);
+                copy_tile<XorRows<CPR>, BN, CPR, THREADS>(V + head, (j + 1) * BN, N, D * 2, lbase + dv, tid, wave);
             }
             if (j >= ntw) return;
             const char* kl = smem + ok;
@@ -304,10 +266,10 @@ struct BwdKV {
             return wave == 0 ? lseh[r] * kLog2e : dlh[r];
         };
         auto issue = [&](int tq, uint32_t st) {
-            copy_tile<T, D, BQ, THREADS>(Q + head, tq * BQ, N, lbase + st, tid, wave);
-            copy_tile<T, D, BQ, THREADS>(dO + head, tq * BQ, N, lbase + st + TILE, tid, wave);
+            copy_tile<XorRows<CPR>, BQ, CPR, THREADS>(Q + head, tq * BQ, N, D * 2, lbase + st, tid, wave);
+            copy_tile<XorRows<CPR>, BQ, CPR, THREADS>(dO + head, tq * BQ, N, D * 2, lbase + st + TILE, tid, wave);
         };
-        copy_tile<T, D, BK, THREADS>(V + head, k0, N, lbase, tid, wave);
+        copy_tile<XorRows<CPR>, BK, CPR, THREADS>(V + head, k0, N, D * 2, lbase, tid, wave);
         float ldv = 0.0f;
         if (t0 < ntq) {
             issue(t0, VBYTES);
@@ -334,7 +296,7 @@ struct BwdKV {
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const x8 vop = *(const x8*)(smem + (vrow * CPR + ((2 * ks + g.h) ^ bswz<CPR>(vrow))) * 16);
+                const x8 vop = *(const x8*)(smem + XorRows<CPR>::slot(vrow, 2 * ks + g.h) * 16);
                 s = VT::mfma(*(const x8*)(ql + g.aoff(0, ks)), kreg[ks], s);
                 dp = VT::mfma(*(const x8*)(gl + g.aoff(0, ks)), vop, dp);
                 if constexpr (D >= 256)

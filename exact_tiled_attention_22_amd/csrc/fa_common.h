@@ -110,24 +110,84 @@ template <> struct Vec<_Float16> {
     }
 };
 
-// ---- output staging: a wave's 32 x D output tile of 2-byte elements through LDS ----
-// The matrix accumulator leaves a lane with 4-column pieces of one row (32 rows per register), so
-// stores straight from registers would touch 32 rows with 8 bytes per lane.  Staged in the wave's own
-// LDS region (row r at r * 2D bytes, 16-byte chunk c at physical chunk c ^ ostage_swz(r)), the tile
-// leaves as whole rows: one 16-byte-per-lane store covers 64 / (D / 8) rows of contiguous output.
-// The swizzle spreads the 16 rows of one 8-byte-per-lane write, and the rows of one 16-byte read,
-// over distinct 16-byte bank groups of the 64-bank LDS.
+// ---- LDS tile layouts ----
+// A tile holds rows of CPR 16-byte chunks.  The LDS serves 16 groups of 16 bytes per clock; the kernels'
+// operand fetches must each hit 16 distinct groups:
+//   * a score-style fetch: 16 lanes read one logical chunk of 16 consecutive rows;
+//   * a transposing fetch (ds_read_b64_tr_*): 32 lanes read 4 logical chunks of 4 consecutive rows
+//     (row % 4 == 0).
+//
+// Row-major rows with an XOR swizzle: chunk c of row r sits at slot r * CPR + (c ^ xswz<CPR>(r)).  Rows
+// of 256 or 512 bytes start in group 0, so the group is the physical chunk mod 16: swapping the two
+// 2-bit halves of (row mod 16) serves both fetches.  Rows of 128 bytes alternate between groups 0
+// and 8, so the parity of the row already separates pairs and 3 bits suffice.
 template <int CPR>
-__device__ __forceinline__ int ostage_swz(int row) {
+__device__ __forceinline__ int xswz(int row) {
     if constexpr (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
     else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
+
+template <int CPR>
+struct XorRows {
+    static constexpr int ROW_CHUNKS = CPR;
+    __device__ static __forceinline__ int slot(int row, int c) { return row * CPR + (c ^ xswz<CPR>(row)); }
+    __device__ static __forceinline__ void row_chunk(int slot, int& row, int& c) {
+        row = slot / CPR;
+        c = (slot % CPR) ^ xswz<CPR>(row);
+    }
+};
+
+// Direct HBM->LDS copy of rows [r0, r0 + ROWS) of a row-major slice of N rows, `stride` bytes apart, of
+// which the first CPR 16-byte chunks are copied into a tile laid out by L, with THREADS threads: copy
+// instruction t of wave w fills LDS slots [t * THREADS + 64 w, + 64).  Rows past N - 1 repeat row N - 1
+// (their results are masked or never stored).  `src` is the slice's first row, `lds` the tile's base.
+template <class L, int ROWS, int CPR, int THREADS>
+__device__ __forceinline__ void copy_tile(const void* __restrict__ src, int r0, int N, int stride, uint32_t lds,
+                                          int tid, int wave) {
+    constexpr int NL = ROWS * CPR / THREADS;
+    static_assert(ROWS * CPR % THREADS == 0, "the tile splits evenly over the threads");
+    const char* base = (const char*)src + (size_t)r0 * stride;
+    const int lim = min(ROWS, N - r0) - 1;  // last row of the slice inside this tile (wave-uniform)
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+        int row, c;
+        L::row_chunk(t * THREADS + tid, row, c);
+        dma16s(base, (uint32_t)(min(row, lim) * stride + c * 16), lds + (uint32_t)((t * THREADS + wave * 64) * 16));
+    }
+}
+
+// The per-thread byte offsets of copy_tile's full-tile copies (the same for every full tile) ...
+template <class L, int ROWS, int CPR, int THREADS>
+__device__ __forceinline__ void tile_offsets(int stride, int tid, uint32_t (&off)[ROWS * CPR / THREADS]) {
+#pragma unroll
+    for (int t = 0; t < ROWS * CPR / THREADS; ++t) {
+        int row, c;
+        L::row_chunk(t * THREADS + tid, row, c);
+        off[t] = (uint32_t)(row * stride + c * 16);
+    }
+}
+
+// ... and a full-tile copy from them: no vector instructions per copy.
+template <int NL, int THREADS>
+__device__ __forceinline__ void copy_tile_full(const void* __restrict__ src_tile, uint32_t lds, int wave,
+                                               const uint32_t (&off)[NL]) {
+#pragma unroll
+    for (int t = 0; t < NL; ++t) dma16s(src_tile, off[t], lds + (uint32_t)((t * THREADS + wave * 64) * 16));
+}
+
+// ---- output staging: a wave's 32 x D output tile of 2-byte elements through LDS ----
+// The matrix accumulator leaves a lane with 4-column pieces of one row (32 rows per register), so
+// stores straight from registers would touch 32 rows with 8 bytes per lane.  Staged in the wave's own
+// LDS region (row r at r * 2D bytes, 16-byte chunk c at physical chunk c ^ xswz(r)), the tile
+// leaves as whole rows: one 16-byte-per-lane store covers 64 / (D / 8) rows of contiguous output.
+// The swizzle (xswz) spreads the 16 rows of one 8-byte-per-lane write, and the rows of one 16-byte read,
+// over distinct 16-byte bank groups of the 64-bank LDS.
 
 // Lane (row n32, half h) writes its 4 elements of columns 8 * chunk + 4 * h + 0..3.
 template <int D, typename X4>
 __device__ __forceinline__ void ostage_put(char* wl, int n32, int h, int chunk, const X4& val) {
     static_assert(sizeof(X4) == 8, "four 2-byte elements");
-    *(X4*)(wl + n32 * (2 * D) + (chunk ^ ostage_swz<D / 8>(n32)) * 16 + h * 8) = val;
+    *(X4*)(wl + n32 * (2 * D) + (chunk ^ xswz<D / 8>(n32)) * 16 + h * 8) = val;
 }
 
 // After every lane of the wave has put its pieces: rows row0 + r (r < 32, row0 + r < nrows) of dst.
@@ -139,7 +199,7 @@ __device__ __forceinline__ void ostage_flush(T* __restrict__ dst, int row0, int 
 #pragma unroll
     for (int i = 0; i < 32 / RPS; ++i) {
         const int r = i * RPS + lane / CPR, c = lane % CPR;
-        const i32x4 val = *(const i32x4*)(wl + r * (2 * D) + (c ^ ostage_swz<CPR>(r)) * 16);
+        const i32x4 val = *(const i32x4*)(wl + r * (2 * D) + (c ^ xswz<CPR>(r)) * 16);
         if (row0 + r < nrows) *(i32x4*)(dst + (size_t)(row0 + r) * D + c * 8) = val;
     }
 }

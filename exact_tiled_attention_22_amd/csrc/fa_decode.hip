@@ -23,12 +23,6 @@ namespace {
 
 constexpr float kTauD = 8.0f;  // lazy rescale threshold (log2 units), as in the forward pass
 
-template <int CPR>
-__device__ __forceinline__ int dswz(int row) {
-    if constexpr (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
-    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
-
 template <typename T, int D, bool CAUSAL>
 struct Decode {
     using VT = Vec<T>;
@@ -41,15 +35,10 @@ struct Decode {
     static constexpr int LDS_BYTES = NW * WAVE_LDS;
     static constexpr int LPT = BN * CPR / 64;             // copies per lane per tile
 
-    // copy rows [r0, r0 + BN) of a [Nk, D] slice into this wave's tile (rows >= Nk repeat row Nk - 1)
+    // copy rows [r0, r0 + BN) of a [Nk, D] slice into this wave's tile (rows >= Nk repeat row Nk - 1),
+    // row-major with the XOR swizzle (fa_common.h); the wave copies alone
     static __device__ __forceinline__ void copy(const T* __restrict__ src, int r0, int Nk, uint32_t lds, int lane) {
-#pragma unroll
-        for (int t = 0; t < LPT; ++t) {
-            const int slot = t * 64 + lane;
-            const int row = slot / CPR;
-            const int c = (slot % CPR) ^ dswz<CPR>(row);
-            dma16(src + (size_t)min(r0 + row, Nk - 1) * D + c * 8, lds + (uint32_t)(t * 64 * 16));
-        }
+        copy_tile<XorRows<CPR>, BN, CPR, 64>(src, r0, Nk, D * 2, lds, lane, 0);
     }
 
     static __device__ __forceinline__ void run(const T* __restrict__ Q, const T* __restrict__ K,
@@ -108,7 +97,7 @@ struct Decode {
             f32x16 s = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const x8 kop = *(const x8*)(kl + (kperm * CPR + ((2 * ks + h) ^ dswz<CPR>(kperm))) * 16);
+                const x8 kop = *(const x8*)(kl + XorRows<CPR>::slot(kperm, 2 * ks + h) * 16);
                 s = VT::mfma(kop, qreg[ks], s);
             }
             if (kv0 + BN > j1 || kv0 + BN - 1 > last_key) {
@@ -148,8 +137,8 @@ struct Decode {
                 for (int sp = 0; sp < 2; ++sp) {
                     const int r0 = sp * 16;
                     const int row0 = r0 + vrow, row1 = r0 + 4 + vrow;
-                    const x4 lo = VT::read_tr(vl + (row0 * CPR + ((cb * 4 + vcc) ^ dswz<CPR>(row0))) * 16 + vb);
-                    const x4 hi = VT::read_tr(vl + (row1 * CPR + ((cb * 4 + vcc) ^ dswz<CPR>(row1))) * 16 + vb);
+                    const x4 lo = VT::read_tr(vl + XorRows<CPR>::slot(row0, cb * 4 + vcc) * 16 + vb);
+                    const x4 hi = VT::read_tr(vl + XorRows<CPR>::slot(row1, cb * 4 + vcc) * 16 + vb);
                     oacc[cb] = VT::mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), sp ? p1 : p0,
                                         oacc[cb]);
                 }

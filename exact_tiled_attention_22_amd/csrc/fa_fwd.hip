@@ -56,19 +56,6 @@ struct Tile {
     static_assert(D > 128 || BM * D * 2 <= LDS_BYTES, "output staging fits the K/V stages");
 };
 
-// XOR swizzle of the 16-byte chunk index inside one LDS row.  The LDS serves 256 bytes per clock
-// (64 banks of 4 bytes = 16 groups of 16 bytes).  Two access patterns must hit 16 distinct groups:
-//   * a score-operand fetch: 16 lanes read one logical chunk of 16 consecutive rows;
-//   * a transposing V fetch: 32 lanes read 4 logical chunks of 4 consecutive rows (row % 4 == 0).
-// Rows of 256 or 512 bytes start in group 0, so the group is the physical chunk mod 16: swapping the
-// two 2-bit halves of (row mod 16) does both.  Rows of 128 bytes alternate between groups 0 and 8, so
-// the parity of the row already separates pairs and 3 bits suffice.
-template <int CPR>
-__device__ __forceinline__ int swz(int row) {
-    if constexpr (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
-    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
-
 // Key split (SPLIT): the workgroups of one query tile each take a contiguous share of its key tiles and
 // write a partial result (O normalised over the share, float32, and lse in base 2; an empty share gives
 // O = 0 and lse = -inf) that a second launch merges.  n = shares per query tile.
@@ -90,44 +77,24 @@ struct Fwd {
     static constexpr int OFF_K0 = TL::OFF_K0, OFF_V0 = TL::OFF_V0, OFF_K1 = TL::OFF_K1, OFF_V1 = TL::OFF_V1;
     static constexpr int NKB = BN / 32;  // 32-key blocks per tile
 
-    // Copy rows [r0, r0 + ROWS) of a [N, D] slice into an LDS tile, ROWS = NLOADS * THREADS / CPR.
-    // Slot s of the tile holds chunk (s % CPR) ^ swz(row) of row s / CPR.  The copies use a scalar
-    // tile base and per-lane 32-bit offsets; a ragged last tile reads row N-1 in place of the missing
-    // rows (they are masked or never stored), through a wave-uniform row limit.
-    // For d <= 128 a full tile takes the lane's byte offsets from foff (the same for every full tile,
-    // computed once by copy_offsets), so it costs no vector instructions; d = 256 has no registers
-    // to spare for them and recomputes the offsets.
+    // K/V tiles: BN rows of CPR chunks, row-major with the XOR swizzle (fa_common.h).  A full tile copies
+    // from the lane's byte offsets in foff (the same for every full tile, computed once), so it costs no
+    // vector instructions for d <= 128; d = 256 has no registers to spare for them and recomputes them;
+    // a ragged last tile reads row N-1 in place of the missing rows (masked or never stored).
+    using Layout = XorRows<CPR>;
     template <int NLOADS>
     static __device__ __forceinline__ void copy_rows(const T* __restrict__ src, int r0, int N, uint32_t lds,
                                                      int tid, int wave, const uint32_t (&foff)[NLOADS]) {
-        constexpr int ROWS = NLOADS * TL::THREADS / CPR;
-        const T* base = src + (size_t)r0 * D;
-        if (D <= 128 && r0 + ROWS <= N) {
-#pragma unroll
-            for (int t = 0; t < NLOADS; ++t)
-                dma16s(base, foff[t], lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
-            return;
-        }
-        const int lim = min(ROWS, N - r0) - 1;  // last row of the slice inside this tile
-#pragma unroll
-        for (int t = 0; t < NLOADS; ++t) {
-            const int slot = t * TL::THREADS + tid;
-            const int row = slot / CPR;
-            const int c = (slot % CPR) ^ swz<CPR>(row);
-            dma16s(base, (uint32_t)((min(row, lim) * D + c * 8) * (int)sizeof(T)),
-                   lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
-        }
+        static_assert(NLOADS * TL::THREADS == BN * CPR, "one tile");
+        if (D <= 128 && r0 + BN <= N)
+            copy_tile_full<NLOADS, TL::THREADS>(src + (size_t)r0 * D, lds, wave, foff);
+        else
+            copy_tile<Layout, BN, CPR, TL::THREADS>(src, r0, N, D * (int)sizeof(T), lds, tid, wave);
     }
 
     template <int NLOADS>
     static __device__ __forceinline__ void copy_offsets(int tid, uint32_t (&foff)[NLOADS]) {
-#pragma unroll
-        for (int t = 0; t < NLOADS; ++t) {
-            const int slot = t * TL::THREADS + tid;
-            const int row = slot / CPR;
-            const int c = (slot % CPR) ^ swz<CPR>(row);
-            foff[t] = (uint32_t)((row * D + c * 8) * (int)sizeof(T));
-        }
+        tile_offsets<Layout, BN, CPR, TL::THREADS>(D * (int)sizeof(T), tid, foff);
     }
 
     // Per-lane geometry of the MFMA operand fetches inside one LDS tile.
@@ -135,11 +102,11 @@ struct Fwd {
         int kperm, h;     // score A-operand: row kperm (+32 for the second key block), chunk 2*ks + h
         int vrow, vcc, vb;  // value A-operand (transposing read): row u*4 + vrow, chunk cb*4 + vcc, byte vb
         __device__ __forceinline__ int koff(int ks) const {
-            return (kperm * CPR + ((2 * ks + h) ^ swz<CPR>(kperm))) * 16;
+            return Layout::slot(kperm, 2 * ks + h) * 16;
         }
         __device__ __forceinline__ int voff(int cb, int u) const {
             const int row = u * 4 + vrow;
-            return (row * CPR + ((cb * 4 + vcc) ^ swz<CPR>(row))) * 16 + vb;
+            return Layout::slot(row, cb * 4 + vcc) * 16 + vb;
         }
     };
 

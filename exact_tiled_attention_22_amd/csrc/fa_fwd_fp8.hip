@@ -62,15 +62,25 @@ struct Tile8 {
     static_assert(BM * D * 2 <= LDS_BYTES, "bf16 output staging fits the workgroup's LDS");
 };
 
-// chunk swizzle of an LDS row (128- or 256-byte rows: 3 bits; 64-byte rows: 2 bits).  Rows read
-// together by one operand fetch differ in (row >> 1) & 3 and in bit 5, rows of equal parity then land
-// in distinct 16-byte bank groups.
+// Tiles of 1-byte elements: row-major rows of CPR 16-byte chunks, chunk c of row r at slot
+// r * CPR + (c ^ swz8(r)) (128- or 256-byte rows: 3 bits; 64-byte rows: 2 bits).  Rows read together by
+// one operand fetch differ in (row >> 1) & 3 and in bit 5, rows of equal parity then land in distinct
+// 16-byte bank groups.  Copied with fa_common.h's copy_tile.
 template <int CPR>
 __device__ __forceinline__ int swz8(int row) {
     int f = (row >> 1) & 3;
     if constexpr (CPR >= 8) f |= ((row >> 5) & 1) << 2;
     return f;
 }
+
+template <int CPR>
+struct Rows8 {
+    __device__ static __forceinline__ int slot(int row, int c) { return row * CPR + (c ^ swz8<CPR>(row)); }
+    __device__ static __forceinline__ void row_chunk(int slot, int& row, int& c) {
+        row = slot / CPR;
+        c = (slot % CPR) ^ swz8<CPR>(row);
+    }
+};
 
 template <int D, bool CAUSAL>
 struct Fwd8 {
@@ -79,37 +89,17 @@ struct Fwd8 {
     static constexpr int KS = D / 64;  // k-steps of the score product
     static constexpr int CB = D / 32;  // 32-column output blocks
 
-    // Copy rows [r0, r0 + ROWS) into an LDS tile (scalar base + lane offsets when every row exists;
-    // a ragged last tile reads row N-1 in place of the missing rows).
+    // Copy rows [r0, r0 + ROWS) into an LDS tile (a ragged last tile reads row N-1 in place of the
+    // missing rows), ROWS = NLOADS * THREADS / CPR.
     template <int NLOADS>
     static __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, int r0, int N, uint32_t lds,
                                                      int tid, int wave) {
-        constexpr int ROWS = NLOADS * TL::THREADS / CPR;
-        if (r0 + ROWS <= N) {
-            const uint8_t* base = src + (size_t)r0 * D;
-#pragma unroll
-            for (int t = 0; t < NLOADS; ++t) {
-                const int slot = t * TL::THREADS + tid;
-                const int row = slot / CPR;
-                const int c = (slot % CPR) ^ swz8<CPR>(row);
-                dma16s(base, (uint32_t)(row * D + c * 16), lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < NLOADS; ++t) {
-                const int slot = t * TL::THREADS + tid;
-                const int row = slot / CPR;
-                const int c = (slot % CPR) ^ swz8<CPR>(row);
-                dma16(src + (size_t)min(r0 + row, N - 1) * D + c * 16,
-                      lds + (uint32_t)((t * TL::THREADS + wave * 64) * 16));
-            }
-        }
+        copy_tile<Rows8<CPR>, NLOADS * TL::THREADS / CPR, CPR, TL::THREADS>(src, r0, N, D, lds, tid, wave);
     }
 
     static __device__ __forceinline__ i32x8 read32(const char* base, int row, int c) {
-        const int sw = swz8<CPR>(row);
-        const i32x4 a = *(const i32x4*)(base + (row * CPR + (c ^ sw)) * 16);
-        const i32x4 b = *(const i32x4*)(base + (row * CPR + ((c + 1) ^ sw)) * 16);
+        const i32x4 a = *(const i32x4*)(base + Rows8<CPR>::slot(row, c) * 16);
+        const i32x4 b = *(const i32x4*)(base + Rows8<CPR>::slot(row, c + 1) * 16);
         return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 
@@ -293,7 +283,7 @@ struct Fwd8 {
                     const int key = vkey + u * 8;
                     const int ch = cb * 2 + vchunk;
                     const i32x2 t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (FA_LDS i32x2*)(vl + (key * CPR + (ch ^ swz8<CPR>(key))) * 16 + vbyte));
+                        (FA_LDS i32x2*)(vl + Rows8<CPR>::slot(key, ch) * 16 + vbyte));
                     vop[2 * u] = t2[0];
                     vop[2 * u + 1] = t2[1];
                 }

@@ -20,13 +20,7 @@ namespace {
 constexpr float kLog2eN = 1.4426950408889634f;
 constexpr float kLn2N = 0.69314718055994531f;
 
-// 16-byte-chunk swizzles of a tile row (CPR chunks per row), as in the fused kernels: a 16-row
-// operand fetch and a transposing fetch each touch 16 distinct bank groups.
-template <int CPR>
-__device__ __forceinline__ int nswz(int row) {
-    if constexpr (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
-    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
+// Tiles are row-major with the XOR chunk swizzle of the fused kernels (XorRows, fa_common.h).
 
 // ---------------------------------------------------------------- 1. scores S = scale * Q K^T
 template <typename T, int D>
@@ -42,13 +36,7 @@ struct Scores {
     // rows [r0, r0 + 128), columns [kc*64, kc*64 + 64) of a [N, D] slice -> one tile (rows >= N repeat N - 1)
     static __device__ __forceinline__ void copy(const T* __restrict__ src, int r0, int N, int kc, uint32_t lds,
                                                 int wave, int lane) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int slot = t * 256 + wave * 64 + lane;
-            const int row = slot >> 3;
-            const int c = (slot & 7) ^ nswz<8>(row);
-            dma16(src + (size_t)min(r0 + row, N - 1) * D + kc * KC + c * 8, lds + (uint32_t)((t * 256 + wave * 64) * 16));
-        }
+        copy_tile<XorRows<8>, BM, 8, 256>(src + kc * KC, r0, N, D * 2, lds, wave * 64 + lane, wave);
     }
 
     static __device__ __forceinline__ void run(const T* __restrict__ Q, const T* __restrict__ K, float* __restrict__ S,
@@ -88,12 +76,12 @@ struct Scores {
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int row = wm * 64 + i * 32 + n32;
-                    a[i] = *(const x8*)(ql + (row * 8 + ((2 * ks + h) ^ nswz<8>(row))) * 16);
+                    a[i] = *(const x8*)(ql + XorRows<8>::slot(row, 2 * ks + h) * 16);
                 }
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int row = wn * 64 + j * 32 + n32;
-                    b[j] = *(const x8*)(kl + (row * 8 + ((2 * ks + h) ^ nswz<8>(row))) * 16);
+                    b[j] = *(const x8*)(kl + XorRows<8>::slot(row, 2 * ks + h) * 16);
                 }
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
@@ -251,21 +239,8 @@ struct PV {
 
     static __device__ __forceinline__ void copy(const T* __restrict__ Ph, const T* __restrict__ Vh, int q0, int k0,
                                                 int N, int ld, uint32_t lds, int wave, int lane) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int slot = t * 256 + wave * 64 + lane;
-            const int row = slot >> 3;
-            const int c = (slot & 7) ^ nswz<8>(row);
-            dma16(Ph + (size_t)min(q0 + row, N - 1) * ld + k0 + c * 8, lds + (uint32_t)((t * 256 + wave * 64) * 16));
-        }
-#pragma unroll
-        for (int t = 0; t < VLPT; ++t) {
-            const int slot = t * 256 + wave * 64 + lane;
-            const int row = slot / CPR;
-            const int c = (slot % CPR) ^ nswz<CPR>(row);
-            dma16(Vh + (size_t)min(k0 + row, N - 1) * D + c * 8,
-                  lds + (uint32_t)(PTILE + (t * 256 + wave * 64) * 16));
-        }
+        copy_tile<XorRows<8>, BM, 8, 256>(Ph + k0, q0, N, ld * 2, lds, wave * 64 + lane, wave);
+        copy_tile<XorRows<CPR>, BN, CPR, 256>(Vh, k0, N, D * 2, lds + PTILE, wave * 64 + lane, wave);
     }
 
     static __device__ __forceinline__ void run(const T* __restrict__ P, const T* __restrict__ V, T* __restrict__ O,
@@ -299,12 +274,12 @@ struct PV {
             // O^T += V^T P^T per 16 keys: lane (n32, h) supplies P[query n32][keys 16 sp + 8 h .. + 7]
 #pragma unroll
             for (int sp = 0; sp < BN / 16; ++sp) {
-                const x8 bp = *(const x8*)(pl + (prow * 8 + ((2 * sp + h) ^ nswz<8>(prow))) * 16);
+                const x8 bp = *(const x8*)(pl + XorRows<8>::slot(prow, 2 * sp + h) * 16);
                 const int row0 = sp * 16 + vrow, row1 = row0 + 4;
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
-                    const x4 lo = VT::read_tr(vl + (row0 * CPR + ((cb * 4 + vcc) ^ nswz<CPR>(row0))) * 16 + vb);
-                    const x4 hi = VT::read_tr(vl + (row1 * CPR + ((cb * 4 + vcc) ^ nswz<CPR>(row1))) * 16 + vb);
+                    const x4 lo = VT::read_tr(vl + XorRows<CPR>::slot(row0, cb * 4 + vcc) * 16 + vb);
+                    const x4 hi = VT::read_tr(vl + XorRows<CPR>::slot(row1, cb * 4 + vcc) * 16 + vb);
                     acc[cb] = VT::mfma(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), bp, acc[cb]);
                 }
             }
