@@ -2,7 +2,7 @@
 """Benchmark of the exact tiled attention forward (and, with --bwd, backward) on one MI355X.
 
 One step = one full forward pass (work partition, Q/K/V tiles, scores, mask, online softmax, P*V,
-epilogue; for the fp8 workload also the three preparation launches) over one batch of seeded
+epilogue; for the fp8 workload also the preparation launch for Q, K and V) over one batch of seeded
 synthetic inputs already resident in HBM.  Default workload: fp16 B1 H8 N16384 d256 causal (the
 largest one-GPU workload).
 With --bwd a step is one backward pass (delta, dQ, dK/dV launches) from the forward's saved o and
@@ -576,9 +576,8 @@ def main() -> int:
         prepped = {}
 
         def prep():
-            prepped["q"] = fa.fp8_prep(qs, signs, w.fp8_block)
-            prepped["k"] = fa.fp8_prep(ks, signs, w.fp8_block)
-            prepped["v"] = fa.fp8_prep(vs, None, w.fp8_block)
+            # one launch quantises Q, K (rotated with the shared signs) and V
+            prepped["q"], prepped["k"], prepped["v"] = fa.fp8_prep_qkv(qs, ks, vs, signs, w.fp8_block)
 
         def fwd8():
             (q8, sq), (k8, sk), (v8, sv) = prepped["q"], prepped["k"], prepped["v"]
@@ -601,7 +600,7 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     # timed region: exactly K back-to-back steps, wall clock and HIP events on the launch stream.  The
-    # e4m3 step holds three preparation launches and the forward kernel: event pairs bracket each
+    # e4m3 step holds the preparation launch and the forward kernel: event pairs bracket each
     # forward launch inside the region, so the roofline covers that kernel alone.
     fp8_fwd = w.dtype == "fp8" and not args.bwd
     ms_per_step, avg_launch_ms = timed_region(step, args.steps, dev, inner=(prep, fwd8) if fp8_fwd else None)
@@ -615,7 +614,7 @@ def main() -> int:
 
     flops = w.flops * (2.5 if args.bwd else 1.0)  # backward: dS, dQ, dK, dV and the recomputed S = 10 N^2 d
     kernel = ("fa_bwd (delta, dQ and dK/dV launches of one call)" if args.bwd else
-              "fa_fwd8_kernel (preparation launches excluded)" if w.dtype == "fp8" else
+              "fa_fwd8_kernel (the preparation launch excluded)" if w.dtype == "fp8" else
               "fa_fwd32_kernel" if w.dtype == "f32" else "fa_fwd16_kernel")
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12

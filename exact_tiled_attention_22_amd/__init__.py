@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     DECODE_NOALLOC_BYTES,
     decode_workspace_bytes,
     fp8_prep,
+    fp8_prep_qkv,
     fwd,
     fwd_decode,
     fwd_decode_noalloc,

@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_naive.restype = i
     L.fa_fp8_prep.argtypes = [vp, i, vp, vp, vp, i, i, i, i, vp]
     L.fa_fp8_prep.restype = i
+    L.fa_fp8_prep_qkv.argtypes = [vp, vp, vp, i] + [vp] * 7 + [i, i, i, i, vp]
+    L.fa_fp8_prep_qkv.restype = i
     L.fa_status_str.argtypes = [i]
     L.fa_status_str.restype = ctypes.c_char_p
     L.fa_last_error.argtypes = []
@@ -421,3 +423,25 @@ def fp8_prep(x, signs=None, block: int = 64, out=None, scales=None):
                            int(block), int(BH), int(N), int(d), _stream(x.device))
     _check(st, "fa_fp8_prep")
     return out, scales
+
+
+def fp8_prep_qkv(q, k, v, signs=None, block: int = 64):
+    """fp8_prep of q, k (rotated with ``signs``, if given) and v (never rotated) in one launch
+    (fa_fp8_prep_qkv).  Returns ((q8, sq), (k8, sk), (v8, sv)), bitwise what three fp8_prep calls give."""
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+            raise ValueError("q, k, v must be contiguous float32/float16/bfloat16 GPU tensors")
+    if q.dim() < 3 or q.shape != k.shape or q.shape != v.shape or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one [..., N, d] shape and dtype")
+    N, d = q.shape[-2], q.shape[-1]
+    BH = int(math.prod(q.shape[:-2]))
+    nblk = -(-N // block) if block > 0 else 0
+    outs = [(torch.empty(q.shape, dtype=torch.float8_e4m3fn, device=q.device),
+             torch.empty(tuple(q.shape[:-2]) + (max(nblk, 0),), dtype=torch.float32, device=q.device)) for _ in range(3)]
+    sign_buf = None if signs is None else _sign_buffer(signs, d)
+    st = lib().fa_fp8_prep_qkv(_ptr(q), _ptr(k), _ptr(v), DTYPE_CODE[q.dtype], *(_ptr(o[0]) for o in outs),
+                               *(_ptr(o[1]) for o in outs),
+                               ctypes.cast(sign_buf, ctypes.c_void_p) if sign_buf is not None else None,
+                               int(block), BH, int(N), int(d), _stream(q.device))
+    _check(st, "fa_fp8_prep_qkv")
+    return tuple(outs)

@@ -157,13 +157,13 @@ __device__ __forceinline__ void hadamard32(float* x, int li, float rs) {
     for (int e = 0; e < kEPL; ++e) x[e] = x[e] * rs;
 }
 
+// One block of `block` rows (block bi of slice bh) by one workgroup.
 template <typename Tin, int D, bool ROT, bool CACHE>
-__global__ __launch_bounds__(kThreads) void fp8_prep_kernel(const Tin* __restrict__ X, uint8_t* __restrict__ X8,
-                                                            float* __restrict__ S, int N, int block, int nblk,
-                                                            float rs, SignMasks sm) {
+__device__ __forceinline__ void prep_block(const Tin* __restrict__ X, uint8_t* __restrict__ X8, float* __restrict__ S,
+                                           int N, int block, int nblk, float rs, const SignMasks& sm, int bh, int bi,
+                                           float* red) {
     constexpr int LPR = D / kEPL;        // lanes per row
     constexpr int RP = kThreads / LPR;   // rows per pass
-    __shared__ float red[kThreads / 64];
     const int tid = threadIdx.x;
     const int li = tid % LPR;            // this lane holds columns li*32 .. li*32+31
     uint32_t mask[16];
@@ -176,7 +176,6 @@ __global__ __launch_bounds__(kThreads) void fp8_prep_kernel(const Tin* __restric
         }
     }
     const int rsub = tid / LPR;          // row within a pass
-    const int bh = blockIdx.x / nblk, bi = blockIdx.x % nblk;
     const int r0 = bi * block;
     const int rows = min(block, N - r0);
     const int passes = (rows + RP - 1) / RP;
@@ -255,6 +254,65 @@ __global__ __launch_bounds__(kThreads) void fp8_prep_kernel(const Tin* __restric
     }
 }
 
+template <typename Tin, int D, bool ROT, bool CACHE>
+__global__ __launch_bounds__(kThreads) void fp8_prep_kernel(const Tin* __restrict__ X, uint8_t* __restrict__ X8,
+                                                            float* __restrict__ S, int N, int block, int nblk,
+                                                            float rs, SignMasks sm) {
+    __shared__ float red[kThreads / 64];
+    prep_block<Tin, D, ROT, CACHE>(X, X8, S, N, block, nblk, rs, sm, blockIdx.x / nblk, blockIdx.x % nblk, red);
+}
+
+// Q, K and V of one attention call in one launch: Q and K rotated with the same signs (when ROT), V
+// not.  Consecutive workgroups take the same block of Q, K and V, so the butterfly-heavy Q and K blocks
+// and the plain V blocks share every CU.
+struct Prep3 {
+    const void* x[3];
+    uint8_t* x8[3];
+    float* s[3];
+};
+
+template <typename Tin, int D, bool ROT, bool CACHE>
+__global__ __launch_bounds__(kThreads) void fp8_prep_qkv_kernel(Prep3 a, int N, int block, int nblk, float rs,
+                                                                SignMasks sm) {
+    __shared__ float red[kThreads / 64];
+    const int t = blockIdx.x % 3, idx = blockIdx.x / 3;
+    const int bh = idx / nblk, bi = idx % nblk;
+    if (t < 2)
+        prep_block<Tin, D, ROT, CACHE>((const Tin*)a.x[t], a.x8[t], a.s[t], N, block, nblk, rs, sm, bh, bi, red);
+    else
+        prep_block<Tin, D, false, CACHE>((const Tin*)a.x[2], a.x8[2], a.s[2], N, block, nblk, rs, sm, bh, bi, red);
+}
+
+template <typename Tin, int D, bool ROT>
+hipError_t launch_prep_qkv_t(const Prep3& a, int block, int BH, int N, float rs, const SignMasks& sm,
+                             hipStream_t stream) {
+    constexpr int RP = kThreads / (D / kEPL);
+    const int nblk = (N + block - 1) / block;
+    const long long nwg = 3LL * BH * nblk;
+    if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
+    if ((block + RP - 1) / RP <= kCachePasses)
+        hipLaunchKernelGGL((fp8_prep_qkv_kernel<Tin, D, ROT, true>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, a,
+                           N, block, nblk, rs, sm);
+    else
+        hipLaunchKernelGGL((fp8_prep_qkv_kernel<Tin, D, ROT, false>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+                           a, N, block, nblk, rs, sm);
+    return hipGetLastError();
+}
+
+template <typename Tin>
+hipError_t launch_prep_qkv_dt(const Prep3& a, bool rot, int block, int BH, int N, int d, float rs,
+                              const SignMasks& sm, hipStream_t stream) {
+    switch (d) {
+        case 64: return rot ? launch_prep_qkv_t<Tin, 64, true>(a, block, BH, N, rs, sm, stream)
+                            : launch_prep_qkv_t<Tin, 64, false>(a, block, BH, N, rs, sm, stream);
+        case 128: return rot ? launch_prep_qkv_t<Tin, 128, true>(a, block, BH, N, rs, sm, stream)
+                             : launch_prep_qkv_t<Tin, 128, false>(a, block, BH, N, rs, sm, stream);
+        case 256: return rot ? launch_prep_qkv_t<Tin, 256, true>(a, block, BH, N, rs, sm, stream)
+                             : launch_prep_qkv_t<Tin, 256, false>(a, block, BH, N, rs, sm, stream);
+        default: return hipErrorNotSupported;
+    }
+}
+
 template <typename Tin, int D, bool ROT>
 hipError_t launch_prep_t(const void* x, void* x8, float* scales, int block, int BH, int N, float rs,
                          const SignMasks& sm, hipStream_t stream) {
@@ -292,10 +350,8 @@ hipError_t launch_prep_dt(const void* x, void* x8, float* scales, bool rot, int 
 
 }  // namespace
 
-hipError_t launch_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, bool rotate,
-                           const uint64_t sign_bits[4], int block, int BH, int N, int d, hipStream_t stream) {
-    // float32 value of 1/sqrt(d): the double quotient rounded once to float
-    const float rs = (float)(1.0 / __builtin_sqrt((double)d));
+namespace {
+SignMasks sign_masks(const uint64_t sign_bits[4]) {
     SignMasks sm{};
     for (int t = 0; t < 256; ++t) {
         if ((sign_bits[t >> 6] >> (t & 63)) & 1) {
@@ -303,6 +359,35 @@ hipError_t launch_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, 
             sm.w[li][e >> 1] |= (e & 1) ? 0x80000000u : 0x00008000u;
         }
     }
+    return sm;
+}
+// float32 value of 1/sqrt(d): the double quotient rounded once to float
+float inv_sqrt_d(int d) { return (float)(1.0 / __builtin_sqrt((double)d)); }
+}  // namespace
+
+hipError_t launch_fp8_prep_qkv(const void* const x[3], int x_dtype, void* const x8[3], float* const scales[3],
+                               bool rotate, const uint64_t sign_bits[4], int block, int BH, int N, int d,
+                               hipStream_t stream) {
+    const SignMasks sm = sign_masks(sign_bits);
+    Prep3 a;
+    for (int t = 0; t < 3; ++t) {
+        a.x[t] = x[t];
+        a.x8[t] = static_cast<uint8_t*>(x8[t]);
+        a.s[t] = scales[t];
+    }
+    const float rs = inv_sqrt_d(d);
+    switch (x_dtype) {
+        case 0: return launch_prep_qkv_dt<float>(a, rotate, block, BH, N, d, rs, sm, stream);
+        case 1: return launch_prep_qkv_dt<_Float16>(a, rotate, block, BH, N, d, rs, sm, stream);
+        case 2: return launch_prep_qkv_dt<__bf16>(a, rotate, block, BH, N, d, rs, sm, stream);
+        default: return hipErrorNotSupported;
+    }
+}
+
+hipError_t launch_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, bool rotate,
+                           const uint64_t sign_bits[4], int block, int BH, int N, int d, hipStream_t stream) {
+    const float rs = inv_sqrt_d(d);
+    const SignMasks sm = sign_masks(sign_bits);
     switch (x_dtype) {
         case 0: return launch_prep_dt<float>(x, x8, scales, rotate, block, BH, N, d, rs, sm, stream);
         case 1: return launch_prep_dt<_Float16>(x, x8, scales, rotate, block, BH, N, d, rs, sm, stream);

@@ -498,15 +498,20 @@ int fa_fwd_naive(const void* q, const void* k, const void* v, void* o, float* ls
     return fa_naive_pv(p, v, o, B, H, N, d, dtype, stream);
 }
 
-int fa_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, const int8_t* hadamard, int block, int BH, int N,
-                int d, void* stream) {
-    g_err[0] = '\0';
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the preparation entry points; fills the sign bit set.  *empty is set for a no-op.
+int prep_check(int x_dtype, const int8_t* hadamard, int block, int BH, int N, int d, uint64_t bits[4], bool* empty,
+               const char* fn) {
+    *empty = false;
     if (x_dtype != FA_F32 && x_dtype != FA_F16 && x_dtype != FA_BF16)
-        return fail(FA_ERR_DTYPE, "fa_fp8_prep input dtype %d (supported: FA_F32, FA_F16, FA_BF16)", x_dtype);
+        return fail(FA_ERR_DTYPE, "%s input dtype %d (supported: FA_F32, FA_F16, FA_BF16)", fn, x_dtype);
     if (BH < 0 || N < 0) return fail(FA_ERR_SHAPE, "negative size BH=%d N=%d", BH, N);
     if (block < 1 || block > 1024) return fail(FA_ERR_ARG, "block must be in 1..1024, got %d", block);
     if (d != 64 && d != 128 && d != 256) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128, 256)", d);
-    uint64_t bits[4] = {0, 0, 0, 0};
+    bits[0] = bits[1] = bits[2] = bits[3] = 0;
     if (hadamard) {
         for (int t = 0; t < d; ++t) {
             if (hadamard[t] == -1)
@@ -515,15 +520,64 @@ int fa_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, const int8_
                 return fail(FA_ERR_ARG, "hadamard[%d] = %d; signs must be +1 or -1", t, static_cast<int>(hadamard[t]));
         }
     }
-    if (BH == 0 || N == 0) return FA_OK;
-    if (int st = check_sizes(BH, N, d)) return st;
+    if (BH == 0 || N == 0) {
+        *empty = true;
+        return FA_OK;
+    }
+    return check_sizes(BH, N, d);
+}
+
+int prep_code(int x_dtype) { return x_dtype == FA_F32 ? 0 : x_dtype == FA_F16 ? 1 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, const int8_t* hadamard, int block, int BH, int N,
+                int d, void* stream) {
+    g_err[0] = '\0';
+    uint64_t bits[4];
+    bool empty = false;
+    if (int st = prep_check(x_dtype, hadamard, block, BH, N, d, bits, &empty, "fa_fp8_prep")) return st;
+    if (empty) return FA_OK;
     if (!x || !x8 || !scales) return fail(FA_ERR_NULL, "x, x8 and scales must be non-NULL");
     if (misaligned(x) || misaligned(x8) || misaligned(scales))
         return fail(FA_ERR_ALIGN, "x, x8 and scales must be 16-byte aligned");
-    const int code = x_dtype == FA_F32 ? 0 : x_dtype == FA_F16 ? 1 : 2;
-    return from_hip(fa::launch_fp8_prep(x, code, x8, scales, hadamard != nullptr, bits, block, BH, N, d,
+    return from_hip(fa::launch_fp8_prep(x, prep_code(x_dtype), x8, scales, hadamard != nullptr, bits, block, BH, N, d,
                                         reinterpret_cast<hipStream_t>(stream)),
                     "fa_fp8_prep");
+}
+
+int fa_fp8_prep_qkv(const void* q, const void* k, const void* v, int x_dtype, void* q8, void* k8, void* v8,
+                    float* q_scales, float* k_scales, float* v_scales, const int8_t* hadamard, int block, int BH,
+                    int N, int d, void* stream) {
+    g_err[0] = '\0';
+    uint64_t bits[4];
+    bool empty = false;
+    if (int st = prep_check(x_dtype, hadamard, block, BH, N, d, bits, &empty, "fa_fp8_prep_qkv")) return st;
+    if (empty) return FA_OK;
+    const void* xs[3] = {q, k, v};
+    void* x8s[3] = {q8, k8, v8};
+    float* ss[3] = {q_scales, k_scales, v_scales};
+    for (int t = 0; t < 3; ++t) {
+        if (!xs[t] || !x8s[t] || !ss[t]) return fail(FA_ERR_NULL, "every input, code and scale pointer must be non-NULL");
+        if (misaligned(xs[t]) || misaligned(x8s[t]) || misaligned(ss[t]))
+            return fail(FA_ERR_ALIGN, "every pointer must be 16-byte aligned");
+    }
+    const int eb = elem_bytes(x_dtype);
+    const size_t in_b = static_cast<size_t>(BH) * N * d * eb, code_b = static_cast<size_t>(BH) * N * d;
+    const size_t sc_b = static_cast<size_t>(BH) * ((N + block - 1) / block) * 4;
+    for (int a = 0; a < 3; ++a) {
+        for (int b = 0; b < 3; ++b) {
+            if (overlaps(x8s[a], code_b, xs[b], in_b) || overlaps(ss[a], sc_b, xs[b], in_b) ||
+                overlaps(ss[a], sc_b, x8s[b], code_b) || (a != b && (overlaps(x8s[a], code_b, x8s[b], code_b) ||
+                                                                     overlaps(ss[a], sc_b, ss[b], sc_b))))
+                return fail(FA_ERR_ARG, "the outputs must not overlap each other or the inputs");
+        }
+    }
+    return from_hip(fa::launch_fp8_prep_qkv(xs, prep_code(x_dtype), x8s, ss, hadamard != nullptr, bits, block, BH, N,
+                                            d, reinterpret_cast<hipStream_t>(stream)),
+                    "fa_fp8_prep_qkv");
 }
 
 }  // extern "C"

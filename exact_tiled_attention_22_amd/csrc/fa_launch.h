@@ -44,6 +44,12 @@ hipError_t launch_fp8_prep(const void* x, int x_dtype, void* x8, float* scales, 
                            const uint64_t sign_bits[4], int block, int BH, int N, int d,
                            hipStream_t stream);
 
+// The same for the Q, K and V of one attention call in one launch: x[0], x[1] (Q, K) rotated when `rotate`,
+// x[2] (V) never; all three [BH, N, d] of x_dtype.
+hipError_t launch_fp8_prep_qkv(const void* const x[3], int x_dtype, void* const x8[3], float* const scales[3],
+                               bool rotate, const uint64_t sign_bits[4], int block, int BH, int N, int d,
+                               hipStream_t stream);
+
 // backward (bf16 / fp16, d in {64, 128, 256}): delta <- rowsum(dout o o), then dq, then dk and dv.
 hipError_t launch_bwd_16(bool is_bf16, const void* q, const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int N, int d,

@@ -165,6 +165,18 @@ int fa_fp8_prep(const void* x, int x_dtype, void* x8, float* scales,
                 const int8_t* hadamard, int block, int BH, int N, int d, void* stream);
 
 /*
+ * fa_fp8_prep of the Q, K and V of one attention call in one launch (FlashAttention-3 article,
+ * "Drei technische Hebel", item 3): q and k are rotated with the same sign vector `hadamard` (or not at
+ * all when it is NULL), v is never rotated; each gets its codes and block scales exactly as fa_fp8_prep
+ * writes them (bitwise).  All three inputs are DEVICE [BH, N, d] of x_dtype; q8, k8, v8 DEVICE [BH, N, d]
+ * bytes; q_scales, k_scales, v_scales DEVICE [BH, ceil(N/block)] float32.  No output may overlap another
+ * output or an input (FA_ERR_ARG).  Validation and errors as fa_fp8_prep.
+ */
+int fa_fp8_prep_qkv(const void* q, const void* k, const void* v, int x_dtype, void* q8, void* k8, void* v8,
+                    float* q_scales, float* k_scales, float* v_scales, const int8_t* hadamard, int block,
+                    int BH, int N, int d, void* stream);
+
+/*
  * Attention of a few queries against a long cached key/value sequence (decode).  The pages tie the
  * method's memory savings to bigger key/value caches and longer context at serving time (Flash
  * Attention glossary, "/02 Warum ist Flash Attention wichtig?").  Same definition as fa_fwd with

@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "fa_bwd", "fa_fwd_decode", "fa_decode_workspace_bytes", "fa_fwd_decode_noalloc",
                           "fa_fp8_prep", "fa_status_str", "fa_last_error", "fa_abi_version",
                           "fa_naive_row_stride", "fa_naive_workspace_bytes", "fa_naive_scores",
-                          "fa_naive_softmax", "fa_naive_pv", "fa_fwd_naive"}
+                          "fa_naive_softmax", "fa_naive_pv", "fa_fwd_naive", "fa_fp8_prep_qkv"}
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
@@ -105,6 +105,33 @@ def test_prep_validation_statuses(lib):
     assert f(big, 2, big * 2, big * 3, ctypes.cast(good, vp), 64, 0, 64, 128, None) == FA_OK
     assert f(None, 2, big * 2, big * 3, ctypes.cast(good, vp), 64, 1, 64, 128, None) == FA_ERR_NULL
     assert f(big + 4, 2, big * 2, big * 3, None, 64, 1, 64, 128, None) == FA_ERR_ALIGN
+
+
+def test_prep_qkv_validation_statuses(lib):
+    f = lib.fa_fp8_prep_qkv
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, vp, vp, ctypes.c_int] + [vp] * 7 + [ctypes.c_int] * 4 + [vp]
+    f.restype = ctypes.c_int
+    big = 1 << 36
+    x = [big * (i + 1) for i in range(3)]         # q k v (fake, never touched)
+    c8 = [big * (i + 4) for i in range(3)]        # q8 k8 v8
+    sc = [big * (i + 7) for i in range(3)]        # scales
+    good = (ctypes.c_int8 * 128)(*([1, -1] * 64))
+    bad = (ctypes.c_int8 * 128)(*([1] * 127 + [0]))
+
+    def call(xx=None, cc=None, ss=None, dtype=2, signs=good, block=64, BH=2, N=100, d=128):
+        return f(*(xx or x), dtype, *(cc or c8), *(ss or sc), signs, block, BH, N, d, None)
+
+    assert call(dtype=3) == FA_ERR_DTYPE
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(block=0) == FA_ERR_ARG
+    assert call(signs=bad) == FA_ERR_ARG
+    assert call(BH=-1) == FA_ERR_SHAPE
+    assert call(cc=[c8[0], None, c8[2]]) == FA_ERR_NULL
+    assert call(ss=[sc[0], sc[1], sc[2] + 4]) == FA_ERR_ALIGN
+    assert call(cc=[c8[0], c8[0], c8[2]]) == FA_ERR_ARG  # q8 and k8 alias
+    assert call(ss=[x[1], sc[1], sc[2]]) == FA_ERR_ARG    # a scale array inside k
+    assert call(N=0) == FA_OK
 
 
 def test_bwd_validation_statuses(lib):

@@ -54,6 +54,27 @@ def test_prep_other_blocks_and_zero_block(block):
     np.testing.assert_array_equal(codes.view(torch.uint8).cpu().numpy(), c_ref)
 
 
+@pytest.mark.parametrize("dtype,d,N,block,rotate", [("bf16", 128, 4096, 64, True), ("bf16", 64, 200, 64, True),
+                                                    ("f16", 256, 333, 64, True), ("f32", 128, 130, 100, False)])
+def test_prep_qkv_one_launch_bitwise(dtype, d, N, block, rotate):
+    # one launch for Q, K (rotated with the shared signs) and V (not rotated): bitwise the three
+    # separate preparations and the oracle's model
+    fa = _fa()
+    q, k, v = gen_qkv(2, 3, N, d, dtype, seed=d + N, outlier_frac=0.001, outlier_mult=20.0)
+    signs = gen_signs(d, seed=d) if rotate else None
+    dev = torch.device("cuda")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    fused = fa.fp8_prep_qkv(qd, kd, vd, signs, block)
+    apart = (fa.fp8_prep(qd, signs, block), fa.fp8_prep(kd, signs, block), fa.fp8_prep(vd, None, block))
+    torch.cuda.synchronize()
+    for name, x, (c8, sc), (a8, asc), sg in zip("qkv", (q, k, v), fused, apart, (signs, signs, None)):
+        assert torch.equal(c8.view(torch.uint8), a8.view(torch.uint8)) and torch.equal(sc, asc), name
+        c_ref, s_ref = fp8_prep_ref(x, sg, block)
+        np.testing.assert_array_equal(c8.view(torch.uint8).cpu().numpy(), c_ref)
+        np.testing.assert_array_equal(sc.cpu().numpy(), s_ref)
+    print(f"prep qkv {dtype} d{d} N{N} block{block} rotate={rotate}: bitwise equal", flush=True)
+
+
 def _rmse(a, b):
     return float(np.sqrt(np.mean((np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64)) ** 2)))
 
