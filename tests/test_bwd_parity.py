@@ -82,6 +82,17 @@ def test_bwd_negative_scale_and_determinism():
     _check(a, attention_bwd_ref(q, k, v, do, False, scale), "negative scale", "bf16")
 
 
+@pytest.mark.parametrize("d,causal", [(64, True), (128, True), (256, False), (256, True)])
+@pytest.mark.parametrize("kind", ["negative", "zero"])
+def test_bwd_negative_and_zero_scale_masks(d, causal, kind):
+    # hidden keys (causal, and the rows past N of a ragged last tile) must get weight 0 whatever the
+    # scale's sign; with scale 0 every visible key of a row gets the same weight
+    q, k, v, do = _inputs(1, 2, 150, d, "bf16", seed=11 + d)
+    scale = -float(np.float32(1 / np.sqrt(d))) if kind == "negative" else 0.0
+    got = _gpu_bwd(q, k, v, do, causal, scale)
+    _check(got, attention_bwd_ref(q, k, v, do, causal, scale), f"{kind} scale d{d} causal={causal}", "bf16")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_full_size_sampled_heads(causal):
     # B16 H16 N1024 d128 in one launch; four heads checked against the oracle
