@@ -237,9 +237,11 @@ __device__ __forceinline__ void prep_block(const Tin* __restrict__ X, uint8_t* _
                 q[w >> 2][w & 3] = wd;
             }
         }
+        // the codes are written once and read by a later launch: non-temporal stores (e4m3 B4 H16 N4096
+        // d128, Q/K/V in one launch: 56.1 -> 50.9 us; non-temporal loads of the input made it slower)
         i32x4* dst = (i32x4*)(X8 + base + (size_t)r * D);
-        dst[0] = q[0];
-        dst[1] = q[1];
+        __builtin_nontemporal_store(q[0], dst);
+        __builtin_nontemporal_store(q[1], dst + 1);
     };
     if constexpr (CACHE) {
 #pragma unroll
