@@ -81,7 +81,9 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ O, con
 }
 
 // ---------------------------------------------------------------------------------------------
-// dQ: one workgroup = 4 waves x 32 query rows; key/value tiles of 64 rows through two LDS stages.
+// dQ: one workgroup = 4 waves x 32 query rows; key/value tiles of 64 rows.  d <= 128 (run_pipe) runs
+// the scores one tile ahead with three K and two V stages; d = 256 (run) takes each tile in order
+// with two stages each (the pipelined form measured slower there).
 template <typename T, int D, bool CAUSAL>
 struct BwdQ {
     using VT = Vec<T>;
@@ -406,8 +408,8 @@ struct BwdQ {
 // kernel (B operand of dP = dO V^T); the K rows of a wave stay in its registers (B operand of
 // S = Q K^T).  Query tiles of 32 rows stream through LDS.  A wave's scores run one tile ahead: the
 // iteration of tile t first computes dP_t while the exponentials of S_t (from the previous
-// iteration) run beside it, then dS_t, then S_{t+1} together with the dV_t and dK_t products, so
-// the exponentials no longer wait for the score MFMAs.  Q therefore has three LDS stages (Q_t for
+// iteration) run beside it, then dS_t, the dV_t and dK_t products, and S_{t+1} right behind them,
+// so the exponentials no longer wait for the score MFMAs.  Q therefore has three LDS stages (Q_t for
 // dK_t, Q_{t+1} for S_{t+1}, Q_{t+2} in flight), dO and lse/D two.  This keeps a wave under 256
 // registers and the workgroup at 72.5 KiB of LDS (d = 128), so two workgroups share a CU.
 // LDS: Q stages 0..2 | dO stages 0..1 | (lse * log2(e) [32], D [32]) stages 0..1 | V [128 rows].
