@@ -115,6 +115,9 @@ def test_fp8_forward_rmse(N, d, causal):
     r_i, _, dl = _fp8_case(1, 2, N, d, causal, seed=N + d)
     assert r_i <= 3e-2
     assert dl <= 1e-3
+    # the kernel's own error budget (rows of a single key or of 64+ keys measure 1.6e-3 .. 5.3e-3; rows
+    # of only a dozen keys, as in the random-shape tests, reach about 8e-3 and keep the format's bar)
+    assert r_i <= 8e-3
 
 
 def test_fp8_forward_unit_scales_and_negative_scale():
