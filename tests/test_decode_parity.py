@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+from bars import LSE_BAR, o_bar
 from oracle import attention_rect
 from synth import gen_qkv
 
@@ -45,6 +46,7 @@ def _check(o, lse, q, k, v, causal, scale, label, heads=None):
     print(f"{label}: max|dO| {wo:.3e} max|dlse| {wl:.3e}", flush=True)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     assert wo <= 1e-2 and wl <= 1e-3
+    assert wo <= o_bar(None, v) and wl <= LSE_BAR  # the dtype's own bar (bars.py)
 
 
 CASES = [

@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 import torch
 
+from bars import LSE_BAR, o_bar
 from oracle import attention_bwd_rows, attention_rows
 from synth import gen_qkv_device
 
@@ -55,6 +56,7 @@ def test_longest_sequence_causal(dtype, d):
     dl = float(np.abs(l_got - l_ref).max())
     print(f"  {len(rows)} rows: max|dO|={do:.3e} max|dlse|={dl:.3e}", flush=True)
     assert do <= TOL_O and dl <= TOL_LSE
+    assert do <= o_bar(dtype, vh) and dl <= LSE_BAR  # the dtype's own bar (bars.py)
 
 
 def test_past_2_31_elements_forward_and_backward():
@@ -78,6 +80,7 @@ def test_past_2_31_elements_forward_and_backward():
         dl = float(np.abs(lse[0, h].cpu().numpy() - l_ref).max())
         line = f"  head {h}: max|dO|={do_:.3e} max|dlse|={dl:.3e}"
         assert do_ <= TOL_O and dl <= TOL_LSE, line
+        assert do_ <= o_bar("bf16", vh) and dl <= LSE_BAR, line
         for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), attention_bwd_rows(qh, kh, vh, gh, True, scale)):
             g = got[0, h].float().cpu().numpy()
             err, top = float(np.abs(g - ref).max()), float(np.abs(ref).max())

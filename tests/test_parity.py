@@ -1,6 +1,7 @@
 """GPU parity of the HIP attention forward against the float64 CPU oracle (through the C ABI).
 
-Tolerances: max|dO| <= 1e-2 and max|dlse| <= 1e-3 for float32/float16/bfloat16 with N(0,1) inputs.
+Tolerances: max|dO| <= 1e-2 and max|dlse| <= 1e-3 for float32/float16/bfloat16 with N(0,1) inputs, and
+each dtype's own bar (bars.py: 2 u max|V| for O, 1e-4 for lse).
 Small shapes are checked element by element; the full-size workloads are run in the launch
 configuration the bench uses and checked on sampled query rows computed one by one by the oracle.
 """
@@ -11,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+from bars import LSE_BAR, o_bar
 from oracle import attention_ref, attention_rows
 from synth import CONFIGS, gen_qkv
 
@@ -38,13 +40,14 @@ def _f32(x):
     return float(np.float32(x))
 
 
-def _compare(o, lse, o_ref, lse_ref, label):
+def _compare(o, lse, o_ref, lse_ref, label, dtype, v):
     do = float(np.abs(o - o_ref).max()) if o.size else 0.0
     dl = float(np.abs(lse - lse_ref).max()) if lse.size else 0.0
-    print(f"{label}: max|dO|={do:.3e} max|dlse|={dl:.3e}", flush=True)
+    bo = o_bar(dtype, v)
+    print(f"{label}: max|dO|={do:.3e} (bar {bo:.1e}) max|dlse|={dl:.3e}", flush=True)
     assert np.isfinite(o).all() and np.isfinite(lse).all(), label
-    assert do <= TOL_O, f"{label}: max|dO| {do}"
-    assert dl <= TOL_LSE, f"{label}: max|dlse| {dl}"
+    assert do <= TOL_O and do <= bo, f"{label}: max|dO| {do}"
+    assert dl <= TOL_LSE and dl <= LSE_BAR, f"{label}: max|dlse| {dl}"
 
 
 SWEEP = [
@@ -65,7 +68,7 @@ def test_shape_sweep(dtype, d, N, causal):
     scale = _f32(1 / math.sqrt(d))
     o, lse = _run(q, k, v, causal, scale)
     o_ref, lse_ref = attention_ref(q, k, v, causal, scale)
-    _compare(o, lse, o_ref, lse_ref, f"{dtype} d{d} N{N} causal={causal}")
+    _compare(o, lse, o_ref, lse_ref, f"{dtype} d{d} N{N} causal={causal}", dtype, v)
 
 
 def test_config1_tiny_fp32_full():
@@ -73,7 +76,7 @@ def test_config1_tiny_fp32_full():
     q, k, v = gen_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=w.cfg_id)
     o, lse = _run(q, k, v, w.causal, w.scale)
     o_ref, lse_ref = attention_ref(q, k, v, w.causal, w.scale)
-    _compare(o, lse, o_ref, lse_ref, w.name)
+    _compare(o, lse, o_ref, lse_ref, w.name, w.dtype, v)
 
 
 @pytest.mark.parametrize("cfg_id", [2, 3, 4])
@@ -102,6 +105,7 @@ def test_full_size_configs_sampled_rows(cfg_id):
           flush=True)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     assert worst_o <= TOL_O and worst_l <= TOL_LSE
+    assert worst_o <= o_bar(w.dtype, v) and worst_l <= LSE_BAR
 
 
 # B*H a multiple of 8: the work partition hands whole heads to each XCD (its remapped branch); several
@@ -120,7 +124,7 @@ def test_xcd_partition_element_wise(dtype, d, B, H, N, causal):
     scale = _f32(1 / math.sqrt(d))
     o, lse = _run(q, k, v, causal, scale)
     o_ref, lse_ref = attention_ref(q, k, v, causal, scale)
-    _compare(o, lse, o_ref, lse_ref, f"{dtype} d{d} B{B} H{H} N{N} causal={causal}")
+    _compare(o, lse, o_ref, lse_ref, f"{dtype} d{d} B{B} H{H} N{N} causal={causal}", dtype, v)
 
 
 # long sequences: 64-bit head offsets, thousands of key tiles per query tile, the longest causal skip
@@ -135,7 +139,8 @@ def test_long_sequence_sampled_rows(dtype, d, N, causal):
     rng = np.random.default_rng(N)
     rows = np.unique(np.concatenate([[0, 1, 63, 64, N // 2, N - 2, N - 1], rng.integers(0, N, 20)]))
     o_ref, lse_ref = attention_rows(q[0, 0], k[0, 0], v[0, 0], rows, causal, scale)
-    _compare(o[0, 0][rows], lse[0, 0][rows], o_ref, lse_ref, f"{dtype} d{d} N{N} causal={causal} ({len(rows)} rows)")
+    _compare(o[0, 0][rows], lse[0, 0][rows], o_ref, lse_ref, f"{dtype} d{d} N{N} causal={causal} ({len(rows)} rows)",
+             dtype, v)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
@@ -162,7 +167,7 @@ def test_zero_and_negative_scale():
     for scale in (0.0, -_f32(1 / math.sqrt(d))):
         o, lse = _run(q, k, v, True, scale)
         o_ref, lse_ref = attention_ref(q, k, v, True, scale)
-        _compare(o, lse, o_ref, lse_ref, f"scale={scale}")
+        _compare(o, lse, o_ref, lse_ref, f"scale={scale}", "bf16", v)
 
 
 def test_bitwise_deterministic_and_non_default_stream():

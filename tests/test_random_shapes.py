@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+from bars import LSE_BAR, o_bar
 from oracle import attention_ref, fp8_attention_ref, fp8_prep_ref
 from synth import gen_qkv, gen_signs
 
@@ -59,6 +60,7 @@ def test_random_shape_16bit(dtype, d, B, H, N, causal, seed):
     print(f"{dtype} d{d} B{B} H{H} N{N} causal={causal}: max|dO|={do:.3e} max|dlse|={dl:.3e}", flush=True)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     assert do <= TOL_O and dl <= TOL_LSE
+    assert do <= o_bar(dtype, v) and dl <= LSE_BAR  # the dtype's own bar (bars.py)
 
 
 @pytest.mark.parametrize("d,H,N,causal,seed", _cases8())

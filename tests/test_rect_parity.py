@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+from bars import LSE_BAR, o_bar
 from oracle import attention_rect
 from synth import gen_qkv
 
@@ -61,6 +62,7 @@ def test_rect_matches_oracle(dtype, d, B, H, Nq, Nk, q_start, causal):
             wl = max(wl, float(np.abs(lse_np[b, h] - lse_ref).max()))
     print(f"  max|dO| {wo:.3e} max|dlse| {wl:.3e}", flush=True)
     assert np.isfinite(o_np).all() and wo <= 1e-2 and wl <= 1e-3
+    assert wo <= o_bar(dtype, v) and wl <= LSE_BAR  # the dtype's own bar (bars.py)
 
 
 @pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, True), ("f16", 64, False), ("f16", 256, True)])
@@ -114,6 +116,7 @@ def test_rect_sharded_long_context_sampled_rows():
             wl = max(wl, float(abs(lse_np[0, h, r] - lse_ref[0])))
     print(f"rect f16 d256 Nq2048 Nk16384 q_start{a}: max|dO| {wo:.3e} max|dlse| {wl:.3e}", flush=True)
     assert np.isfinite(o_np).all() and wo <= 1e-2 and wl <= 1e-3
+    assert wo <= o_bar("f16", v) and wl <= LSE_BAR
 
 
 def test_rect_rejects_bad_start():

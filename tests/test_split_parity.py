@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+from bars import LSE_BAR, o_bar
 from oracle import attention_rect
 from synth import gen_qkv
 
@@ -66,6 +67,7 @@ def test_split_matches_oracle(dtype, d, B, H, Nq, Nk, q_start, causal, nsplit):
           f"max|dO|={worst_o:.3e} max|dlse|={worst_l:.3e}", flush=True)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     assert worst_o <= TOL_O and worst_l <= TOL_LSE
+    assert worst_o <= o_bar(dtype, v) and worst_l <= LSE_BAR  # the dtype's own bar (bars.py)
 
 
 @pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, True), ("f16", 64, False), ("f16", 256, True)])
@@ -117,3 +119,4 @@ def test_sequence_share_full_size_sampled_rows():
           f"max|dlse|={worst_l:.3e}", flush=True)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     assert worst_o <= TOL_O and worst_l <= TOL_LSE
+    assert worst_o <= o_bar("f16", v) and worst_l <= LSE_BAR
