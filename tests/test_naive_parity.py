@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+from bars import LSE_BAR, o_bar
 from oracle import attention_probs, attention_ref, attention_rows
 from synth import gen_qkv
 
@@ -65,6 +66,7 @@ def test_naive_stages_and_output(dtype, d, B, H, N, causal):
     print(f"naive {dtype} d{d} B{B} H{H} N{N} causal={causal}: max|dS| {ws:.2e} max|dP| {wp:.2e} "
           f"max|dO| {wo:.3e} max|dlse| {wl:.3e}", flush=True)
     assert np.isfinite(o_np).all() and wo <= 1e-2 and wl <= 1e-3
+    assert wo <= o_bar(dtype, v) and wl <= LSE_BAR  # the dtype's own bar (bars.py)
 
 
 # rows longer than 8192 take the two-pass softmax; full-size workloads are checked on sampled rows
@@ -95,3 +97,4 @@ def test_naive_sampled_rows(dtype, d, B, H, N, causal):
           f"max|dO| {wo:.3e} max|dlse| {wl:.3e}", flush=True)
     assert np.isfinite(o_np).all() and np.isfinite(lse_np).all()
     assert wo <= 1e-2 and wl <= 1e-3
+    assert wo <= o_bar(dtype, v) and wl <= LSE_BAR  # the dtype's own bar (bars.py)
