@@ -118,3 +118,43 @@ def test_split_replay_bitwise():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1]), f"split replay {rep} differs"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_prep_and_forward_replay_bitwise(causal):
+    # the e4m3 path: three preparation launches (Q and K rotated) and the e4m3 forward, all into the
+    # caller's buffers; codes, scales, output and lse overwritten between replays
+    from synth import gen_signs
+
+    fa = _fa()
+    dev = torch.device("cuda")
+    B, H, N, d = 2, 2, 300, 128
+    q, k, v = (t.to(dev) for t in gen_qkv(B, H, N, d, "bf16", seed=46, outlier_frac=0.001, outlier_mult=20.0))
+    signs = gen_signs(d, seed=d)
+    nblk = -(-N // 64)
+    codes = [torch.empty(q.shape, dtype=torch.float8_e4m3fn, device=dev) for _ in range(3)]
+    scales = [torch.empty((B, H, nblk), dtype=torch.float32, device=dev) for _ in range(3)]
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    def step():
+        for x, sg, c, s in zip((q, k, v), (signs, signs, None), codes, scales):
+            fa.fp8_prep(x, sg, 64, out=c, scales=s)
+        fa.fwd(*codes, causal=causal, fp8_scales=tuple(scales), out=o, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (*codes, *scales, o, lse)]
+    graph = _capture(step)
+    for rep in range(3):
+        for c in codes:
+            c.view(torch.uint8).fill_(0x7F)  # e4m3 NaN codes
+        for t in (*scales, o, lse):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (*codes, *scales, o, lse)
+        for i, (g, w) in enumerate(zip(got, ref)):
+            same = torch.equal(g.view(torch.uint8), w.view(torch.uint8)) if g.dtype == torch.float8_e4m3fn else torch.equal(g, w)
+            assert same, f"fp8 replay {rep}: output {i} differs from the eager result"
