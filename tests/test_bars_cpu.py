@@ -15,3 +15,12 @@ def test_o_bar_formula_cap_and_dtypes():
     assert o_bar(None, v.to(torch.bfloat16)) == o_bar("bf16", v)
     assert o_bar("f16", torch.zeros(0)) == 1e-5
     assert LSE_BAR < STATED_LSE
+
+
+def test_o_bound_is_the_uncapped_formula():
+    from bars import o_bound
+
+    v = torch.tensor([4.5, -1.0])
+    assert abs(o_bound("bf16", v) - (2 * 2.0 ** -8 * 4.5 + 1e-5)) < 1e-12
+    assert o_bar("bf16", v) == STATED_O < o_bound("bf16", v)
+    assert o_bound("f16", v) == o_bar("f16", v)
