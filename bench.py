@@ -5,7 +5,7 @@ One step = one full forward pass (work partition, Q/K/V tiles, scores, mask, onl
 epilogue; for the fp8 workload also the preparation launch for Q, K and V) over one batch of seeded
 synthetic inputs already resident in HBM.  Default workload: fp16 B1 H8 N16384 d256 causal (the
 largest one-GPU workload).
-With --bwd a step is one backward pass (delta, dQ, dK/dV launches) from the forward's saved o and
+With --bwd a step is one backward pass (the dQ launch, which also forms D, then dK/dV) from the forward's saved o and
 lse, counted as 10*B*H*N^2*d flops (/2 causal).  --decode times the decode path (K/V cache read
 GB/s); --naive times the unfused path (scores, softmax, P*V through HBM) beside the fused kernel.
 
@@ -613,7 +613,7 @@ def main() -> int:
         cold_ms = cold_launch_ms(step, 20, dev)
 
     flops = w.flops * (2.5 if args.bwd else 1.0)  # backward: dS, dQ, dK, dV and the recomputed S = 10 N^2 d
-    kernel = ("fa_bwd (delta, dQ and dK/dV launches of one call)" if args.bwd else
+    kernel = ("fa_bwd (dQ and dK/dV launches of one call)" if args.bwd else
               "fa_fwd8_kernel (the preparation launch excluded)" if w.dtype == "fp8" else
               "fa_fwd32_kernel" if w.dtype == "f32" else "fa_fwd16_kernel")
     value = flops / (ms_per_step * 1e-3) / 1e12

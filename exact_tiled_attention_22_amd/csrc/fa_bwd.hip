@@ -7,11 +7,11 @@
 //     P = exp(scale Q K^T - lse)   (visible keys),   D_i = sum_t dO[i,t] O[i,t],
 //     dS = P o (dO V^T - D),   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
 // Like the forward pass it never stores an N x N matrix: P and dS are rebuilt tile by tile from Q,
-// K and lse.  Three launches, no atomics (the result is deterministic):
-//   1. delta_kernel: D = rowsum(dO o O), float32 [B,H,N] in a caller-provided buffer;
-//   2. BwdQ: one workgroup per 128 query rows streams the K/V tiles (as the forward pass does) and
-//      accumulates dQ^T = K^T dS^T in registers;
-//   3. BwdKV: one workgroup per 128 keys (V rows held in LDS, K rows in registers) streams the Q/dO
+// K and lse.  Two launches, no atomics (the result is deterministic):
+//   1. BwdQ: one workgroup per 128 query rows first forms D = rowsum(dO o O) for its rows (writing it
+//      to a caller-provided float32 [B,H,N] buffer), then streams the K/V tiles (as the forward pass
+//      does) and accumulates dQ^T = K^T dS^T in registers;
+//   2. BwdKV: one workgroup per 128 keys (V rows held in LDS, K rows in registers) streams the Q/dO
 //      tiles (with their lse and D) and accumulates dV^T = dO^T P and dK^T = Q^T dS in registers.
 // Operand conventions are the forward pass's: v_mfma_f32_32x32x16 with the A-operand rows permuted
 // so that 8 consecutive accumulator registers of a lane hold 8 consecutive rows (keys in BwdQ,
@@ -60,24 +60,27 @@ __device__ __forceinline__ int opaque(int x) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// D = rowsum(dO o O) in float32: D/8 lanes per row, 16-byte loads, a butterfly sum over the row's lanes.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ O, const T* __restrict__ dO,
-                                                    float* __restrict__ Dl, long long rows) {
+// D = rowsum(dO o O) in float32 for this lane's query row.  Lane (n32, h) holds the row's 16-byte
+// chunks 2 ks + h (ks < KS) of dO in dreg and reads the same chunks of O.  Each chunk is a chain of
+// fused multiply-adds; the chunk sums then combine as a butterfly from the widest distance down (chunk
+// distance D/16 ... 2 inside the lane, distance 1 across the two wave halves), one fixed order.
+template <typename T, int KS>
+__device__ __forceinline__ float row_delta(const T* __restrict__ orow, int h, const typename Vec<T>::x8 (&dreg)[KS]) {
     using x8 = typename Vec<T>::x8;
-    constexpr int LPR = D / 8, RPB = 256 / LPR;
-    const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
-    const int li = threadIdx.x % LPR;
-    float acc = 0.0f;
-    if (row < rows) {
-        const x8 o = *(const x8*)(O + row * D + li * 8);
-        const x8 g = *(const x8*)(dO + row * D + li * 8);
+    float p[KS];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
+    for (int ks = 0; ks < KS; ++ks) {
+        const x8 o = *(const x8*)(orow + ks * 16 + h * 8);
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = __builtin_fmaf((float)o[e], (float)dreg[ks][e], a);
+        p[ks] = a;
     }
 #pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (li == 0 && row < rows) Dl[row] = acc;
+    for (int off = KS / 2; off >= 1; off >>= 1)
+#pragma unroll
+        for (int ks = 0; ks < off; ++ks) p[ks] = p[ks] + p[ks + off];
+    return halves_sum(p[0]);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -99,9 +102,9 @@ struct BwdQ {
 
     static __device__ __forceinline__ void run(const T* __restrict__ Q, const T* __restrict__ K,
                                                const T* __restrict__ V, const T* __restrict__ dO,
-                                               const float* __restrict__ LSE, const float* __restrict__ Dl,
-                                               T* __restrict__ dQ, int N, int BH, int ntq, float c, float scale,
-                                               char* smem) {
+                                               const T* __restrict__ O, const float* __restrict__ LSE,
+                                               float* __restrict__ Dl, T* __restrict__ dQ, int N, int BH, int ntq,
+                                               float c, float scale, char* smem) {
         const int tid = threadIdx.x, lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int n32 = lane & 31, h = lane >> 5;
@@ -122,7 +125,9 @@ struct BwdQ {
             dreg[ks] = *(const x8*)(dO + head + (size_t)qrow * D + ks * 16 + h * 8);
         }
         const float lse2 = LSE[(size_t)bh * N + qrow] * kLog2e;
-        const float dd = Dl[(size_t)bh * N + qrow];
+        // D for this row, written once (by the lower wave half) for the dK/dV kernel
+        const float dd = row_delta<T, KS>(O + head + (size_t)qrow * D, h, dreg);
+        if (h == 0 && query < N) Dl[(size_t)bh * N + query] = dd;
         copy_tile<XorRows<CPR>, BN, CPR, THREADS>(K + head, 0, N, D * 2, lbase, tid, wave);
         copy_tile<XorRows<CPR>, BN, CPR, THREADS>(V + head, 0, N, D * 2, lbase + TILE, tid, wave);
 
@@ -227,9 +232,9 @@ struct BwdQ {
     // V two.  80 KiB of LDS at d = 128, two workgroups per CU.
     static __device__ __forceinline__ void run_pipe(const T* __restrict__ Q, const T* __restrict__ K,
                                                     const T* __restrict__ V, const T* __restrict__ dO,
-                                                    const float* __restrict__ LSE, const float* __restrict__ Dl,
-                                                    T* __restrict__ dQ, int N, int BH, int ntq, float c,
-                                                    float scale, char* smem) {
+                                                    const T* __restrict__ O, const float* __restrict__ LSE,
+                                                    float* __restrict__ Dl, T* __restrict__ dQ, int N, int BH,
+                                                    int ntq, float c, float scale, char* smem) {
         const int tid = threadIdx.x, lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int n32 = lane & 31, h = lane >> 5;
@@ -258,7 +263,9 @@ struct BwdQ {
             dreg[ks] = *(const x8*)(dO + head + (size_t)qrow * D + ks * 16 + h * 8);
         }
         const float lse2 = LSE[(size_t)bh * N + qrow] * kLog2e;
-        const float dd = Dl[(size_t)bh * N + qrow];
+        // D for this row, written once (by the lower wave half) for the dK/dV kernel
+        const float dd = row_delta<T, KS>(O + head + (size_t)qrow * D, h, dreg);
+        if (h == 0 && query < N) Dl[(size_t)bh * N + query] = dd;
         auto copy_k = [&](int j, int st) {
             copy_tile<XorRows<CPR>, BN, CPR, THREADS>(K + head, j * BN, N, D * 2, lbase + st * TILE, tid, wave);
         };
@@ -661,14 +668,14 @@ struct BwdKV {
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_q_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                        const T* __restrict__ V, const T* __restrict__ dO,
-                                                       const float* __restrict__ LSE, const float* __restrict__ Dl,
-                                                       T* __restrict__ dQ, int N, int BH, int ntq, float c,
-                                                       float scale) {
+                                                       const T* __restrict__ O, const float* __restrict__ LSE,
+                                                       float* __restrict__ Dl, T* __restrict__ dQ, int N, int BH,
+                                                       int ntq, float c, float scale) {
     __shared__ __attribute__((aligned(1024))) char smem[BwdQ<T, D, CAUSAL>::LDS_BYTES];
     if constexpr (BwdQ<T, D, CAUSAL>::PIPE)
-        BwdQ<T, D, CAUSAL>::run_pipe(Q, K, V, dO, LSE, Dl, dQ, N, BH, ntq, c, scale, smem);
+        BwdQ<T, D, CAUSAL>::run_pipe(Q, K, V, dO, O, LSE, Dl, dQ, N, BH, ntq, c, scale, smem);
     else
-        BwdQ<T, D, CAUSAL>::run(Q, K, V, dO, LSE, Dl, dQ, N, BH, ntq, c, scale, smem);
+        BwdQ<T, D, CAUSAL>::run(Q, K, V, dO, O, LSE, Dl, dQ, N, BH, ntq, c, scale, smem);
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -685,12 +692,9 @@ template <typename T, int D, bool CAUSAL>
 hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o, const float* lse,
                         const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int N, float scale,
                         hipStream_t stream) {
-    const long long rows = (long long)BH * N;
-    constexpr int RPB = 256 / (D / 8);
-    const long long nd = (rows + RPB - 1) / RPB;
     const int ntq = (N + BwdQ<T, D, CAUSAL>::BM - 1) / BwdQ<T, D, CAUSAL>::BM;
     const int nkt = (N + BwdKV<T, D, CAUSAL>::BK - 1) / BwdKV<T, D, CAUSAL>::BK;
-    if (nd > 0x7fffffffLL || (long long)BH * ntq > 0x7fffffffLL || (long long)BH * nkt > 0x7fffffffLL)
+    if ((long long)BH * ntq > 0x7fffffffLL || (long long)BH * nkt > 0x7fffffffLL)
         return hipErrorInvalidValue;
     // c keeps its sign and at least 1e-30 of magnitude, so that a masked score (set to -inf, or +inf
     // when c < 0) gives an exponent of -inf; below that magnitude every weight rounds as it does for
@@ -698,14 +702,11 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
     float c = scale * kLog2e;
     if (std::signbit(c)) c = fminf(c, -1e-30f);
     else c = fmaxf(c, 1e-30f);
-    hipLaunchKernelGGL((delta_kernel<T, D>), dim3((unsigned)nd), dim3(256), 0, stream, (const T*)o, (const T*)dout,
-                       delta, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // the dQ launch writes D, which the dK/dV launch after it on the stream reads
     hipLaunchKernelGGL((bwd_q_kernel<T, D, CAUSAL>), dim3((unsigned)(BH * ntq)), dim3(256), 0, stream, (const T*)q,
-                       (const T*)k, (const T*)v, (const T*)dout, lse, (const float*)delta, (T*)dq, N, BH, ntq, c,
+                       (const T*)k, (const T*)v, (const T*)dout, (const T*)o, lse, delta, (T*)dq, N, BH, ntq, c,
                        scale);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_kv_kernel<T, D, CAUSAL>), dim3((unsigned)(BH * nkt)), dim3(256), 0, stream, (const T*)q,
                        (const T*)k, (const T*)v, (const T*)dout, lse, (const float*)delta, (T*)dk, (T*)dv, N, BH,
