@@ -97,14 +97,35 @@ struct Fwd {
         tile_offsets<Layout, BN, CPR, TL::THREADS>(D * (int)sizeof(T), tid, foff);
     }
 
-    // Per-lane geometry of the MFMA operand fetches inside one LDS tile.
+    // Per-lane geometry of the MFMA operand fetches inside one LDS tile.  With 32-chunk rows (d = 256)
+    // the swizzle changes only the low four bits of a chunk index, so chunks 16 apart sit 256 bytes
+    // apart in every row: the offsets of the upper half are those of the lower half plus an immediate,
+    // and eight address registers serve the sixteen score k-steps (four serve the eight value blocks
+    // of each row group).  That keeps the non-causal d = 256 kernel within its registers (7 spilled
+    // before; fp16 B2 H8 N4096 266.8 -> 254.6 us, bitwise the same); the causal instances measured 2-6 %
+    // slower with it (their 4 spilled values sit outside the tile loop) and keep one register per offset.
     struct Lane {
         int kperm, h;     // score A-operand: row kperm (+32 for the second key block), chunk 2*ks + h
         int vrow, vcc, vb;  // value A-operand (transposing read): row u*4 + vrow, chunk cb*4 + vcc, byte vb
+        static constexpr bool HALVES = CPR >= 32 && !CAUSAL;
+        int ko[HALVES ? 8 : 1], vo[HALVES ? 2 : 1][HALVES ? 4 : 1];
+        __device__ __forceinline__ void init() {
+            if constexpr (HALVES) {
+                static_assert(Layout::ROW_CHUNKS == 32, "the upper 16 chunks of a row keep their order");
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ko[i] = Layout::slot(kperm, 2 * i + h) * 16;
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) vo[u][i] = Layout::slot(u * 4 + vrow, i * 4 + vcc) * 16 + vb;
+            }
+        }
         __device__ __forceinline__ int koff(int ks) const {
-            return Layout::slot(kperm, 2 * ks + h) * 16;
+            if constexpr (HALVES) return ko[ks & 7] + (ks >> 3) * 256;
+            else return Layout::slot(kperm, 2 * ks + h) * 16;
         }
         __device__ __forceinline__ int voff(int cb, int u) const {
+            if constexpr (HALVES) return vo[u][cb & 3] + (cb >> 2) * 256;
             const int row = u * 4 + vrow;
             return Layout::slot(row, cb * 4 + vcc) * 16 + vb;
         }
@@ -455,6 +476,7 @@ struct Fwd {
             ln.vcc = (G & 1) * 2 + ((i16 & 3) >> 1);
             ln.vb = (i16 & 1) * 8;
         }
+        ln.init();
         uint32_t foff[LPT];
         copy_offsets<LPT>(tid, foff);
         // Q operand straight from HBM (the first iteration's wait covers these loads and the copies)
@@ -565,6 +587,7 @@ struct Fwd {
             ln.vcc = (G & 1) * 2 + ((i16 & 3) >> 1);
             ln.vb = (i16 & 1) * 8;
         }
+        ln.init();
 
         uint32_t foff[LPT];
         copy_offsets<LPT>(tid, foff);
