@@ -1,6 +1,6 @@
 """Ragged-tail sweeps on the GPU, each case against the float64 oracle.
 
-The tile loops meet a partial last tile of keys (64 keys for d <= 128, 32 for d = 256) and a partial last
+The tile loops meet a partial last tile of keys (64 keys for 16-bit d <= 128, 32 for d = 256 and float32) and a partial last
 tile of query rows; the backward kernels unroll six tiles and finish with a guarded tail.  These sweeps
 walk every sequence length up to a little past one tile (so every residue of the key-tile size) for the
 forward, and sequence lengths whose tile counts cover every position of the six-tile unroll for the
@@ -53,6 +53,27 @@ def test_forward_every_tail_length(dtype, d, causal, Ns):
         worst_o, worst_l = max(worst_o, do), max(worst_l, dl)
     print(f"{dtype} d{d} causal={causal} N {Ns.start}..{Ns.stop - 1}: worst max|dO|={worst_o:.3e} "
           f"max|dlse|={worst_l:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("d,causal", [(64, False), (64, True), (128, False), (128, True), (256, True)])
+def test_fp32_forward_tail_lengths(d, causal):
+    # float32 kernel: 32-key tiles and 128-row query tiles; N = 1..70 meets every residue of the key tile
+    # (twice), and the lengths around 128 and 256 the partial and full second and third query tiles
+    fa = _fa()
+    dev = torch.device("cuda")
+    worst_o = worst_l = 0.0
+    for N in list(range(1, 71)) + [126, 127, 128, 129, 130, 255, 256, 257]:
+        q, k, v = gen_qkv(1, 2, N, d, "f32", seed=13 * N + d)
+        o, lse = fa.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=_scale(d))
+        torch.cuda.synchronize()
+        o, lse = o.cpu().numpy(), lse.cpu().numpy()
+        o_ref, lse_ref = attention_ref(q, k, v, causal, _scale(d))
+        do, dl = float(np.abs(o - o_ref).max()), float(np.abs(lse - lse_ref).max())
+        label = f"f32 d{d} causal={causal} N{N}: max|dO|={do:.3e} max|dlse|={dl:.3e}"
+        assert np.isfinite(o).all() and np.isfinite(lse).all(), label
+        assert do <= o_bar("f32", v) and dl <= LSE_BAR, label
+        worst_o, worst_l = max(worst_o, do), max(worst_l, dl)
+    print(f"f32 d{d} causal={causal}: worst max|dO|={worst_o:.3e} max|dlse|={worst_l:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("causal", [False, True])
