@@ -103,6 +103,33 @@ def test_fp8_forward_every_tail_length(causal):
     print(f"e4m3 d{d} causal={causal} N 1..129: worst RMSE {worst:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("d,causal", [(64, False), (64, True), (256, False), (256, True)])
+def test_fp8_forward_tail_lengths_other_dims(d, causal):
+    # 64-key tiles; 128-row (d = 64) and 256-row (d = 256) query tiles
+    fa = _fa()
+    dev = torch.device("cuda")
+    signs = gen_signs(d, seed=d)
+    worst = 0.0
+    for N in list(range(1, 71)) + [127, 128, 129, 255, 256, 257]:
+        q, k, v = gen_qkv(1, 2, N, d, "bf16", seed=19 * N + d, outlier_frac=0.001, outlier_mult=20.0)
+        q8, sq = fa.fp8_prep(q.to(dev), signs, 64)
+        k8, sk = fa.fp8_prep(k.to(dev), signs, 64)
+        v8, sv = fa.fp8_prep(v.to(dev), None, 64)
+        o, lse = fa.fwd(q8, k8, v8, causal=causal, scale=_scale(d), fp8_scales=(sq, sk, sv))
+        torch.cuda.synchronize()
+        cq, csq = fp8_prep_ref(q, signs, 64)
+        ck, csk = fp8_prep_ref(k, signs, 64)
+        cv, csv = fp8_prep_ref(v, None, 64)
+        o_ref, lse_ref = fp8_attention_ref(cq, csq, ck, csk, cv, csv, 64, causal, _scale(d))
+        o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+        rmse = float(np.sqrt(np.mean((o.astype(np.float64) - o_ref) ** 2)))
+        dl = float(np.abs(lse - lse_ref).max())
+        label = f"e4m3 d{d} causal={causal} N{N}: RMSE {rmse:.3e} max|dlse|={dl:.3e}"
+        assert np.isfinite(o).all() and rmse <= 3e-2 and dl <= 1e-3, label
+        worst = max(worst, rmse)
+    print(f"e4m3 d{d} causal={causal}: worst RMSE {worst:.3e}", flush=True)
+
+
 def _bwd_lengths(t_max):
     # 32-row query tiles (dK/dV loop) and 64-key tiles (dQ loop): t full tiles plus 1 or 31 rows
     return sorted({32 * t + r for t in range(t_max) for r in (1, 31)})
