@@ -113,8 +113,10 @@ struct Decode {
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
             const float mt = halves_max(mx) * c;
             if (__ballot(mt > m_run + kTauD)) {
+                // a query that has seen no key of the chunk yet keeps m = -inf while another lane of
+                // the wave raises its maximum: its factor is 1, not 2^(-inf - -inf)
                 const float mn = fmaxf(m_run, mt);
-                const float alpha = fast_exp2(m_run - mn);
+                const float alpha = m_run == mn ? 1.0f : fast_exp2(m_run - mn);
                 m_run = mn;
                 l_run *= alpha;
 #pragma unroll

@@ -397,10 +397,14 @@ struct Fwd {
     // Walking its keys from its diagonal down to key 0, every workgroup of such a round (an odd one)
     // reaches a given key tile at the same time as the others on its XCD, which then read it through the
     // XCD's L2 once instead of once per workgroup; even rounds start together and walk upward.  (The
-    // online softmax is independent of the key order.)  Key shares and non-causal grids walk upward.
-    static __device__ __forceinline__ bool keys_down(int cap) {
+    // online softmax is independent of the key order.)  Key shares and non-causal grids walk upward, and
+    // so do queries placed at a position qpos that is not a multiple of 32: walking down, a wave's first
+    // tile is the one holding its last row's key, and only with 32-aligned rows does every row of the
+    // wave see a key of that tile (a row that sees none would keep a running maximum of -inf while
+    // others raise theirs, and the correction factor 2^(-inf - -inf) is not a number).
+    static __device__ __forceinline__ bool keys_down(int cap, int qpos) {
         if constexpr (!CAUSAL || SPLIT) return false;
-        return ((blockIdx.x >> 3) / cap) & 1;
+        return (qpos & 31) == 0 && (((blockIdx.x >> 3) / cap) & 1);
     }
 
     // Block id -> (bh, query tile, key share); the shares of a query tile sit nbase ids apart, so with
@@ -465,7 +469,7 @@ struct Fwd {
         }
         // tiles this wave computes: [jb, ntw); iteration j handles key tile kt(j)
         const int ntw = min(je, ((CAUSAL ? min(Nk, qpos + q0w + QW) : Nk) + BN - 1) / BN);
-        const bool down = keys_down(cap);
+        const bool down = keys_down(cap, qpos);
         auto kt = [&](int j) { return down ? jb + je - 1 - j : j; };
         Lane ln;
         ln.kperm = ((n32 >> 4) & 1) * 16 + ((n32 >> 2) & 1) * 8 + ((n32 >> 3) & 1) * 4 + (n32 & 3);
@@ -575,7 +579,7 @@ struct Fwd {
         }
         // tiles this wave computes: [jb, ntw); iteration j handles key tile kt(j)
         const int ntw = min(je, ((CAUSAL ? min(Nk, qpos + q0w + QW) : Nk) + BN - 1) / BN);
-        const bool down = keys_down(cap);
+        const bool down = keys_down(cap, qpos);
         auto kt = [&](int j) { return down ? jb + je - 1 - j : j; };
 
         Lane ln;

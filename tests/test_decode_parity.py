@@ -95,3 +95,15 @@ def test_decode_large_cache_sampled_heads():
     rng = np.random.default_rng(1)
     heads = {divmod(int(x), 32) for x in rng.choice(256, size=4, replace=False)}
     _check(o, lse, q, k, v, False, scale, "B8 H32 Nq1 Nk32768", heads=heads)
+
+
+@pytest.mark.parametrize("d,Nq,causal", [(64, 1, True), (128, 1, False), (256, 1, True), (64, 4, False),
+                                         (128, 4, True), (256, 4, False)])
+def test_decode_every_tail_length(d, Nq, causal):
+    # key lengths Nq..Nq+69 (one chunk: every residue of the 32-key tile, twice) and a band where the keys
+    # are split over several chunks with ragged ends; the vector kernel (Nq = 1) and the matrix kernel
+    scale = float(np.float32(1 / np.sqrt(d)))
+    for Nk in list(range(Nq, Nq + 70)) + list(range(4090, 4100)):
+        q, k, v = _inputs(1, 2, Nq, Nk, d, "bf16", seed=3 * Nk + d + Nq)
+        o, lse = _run(q, k, v, causal, scale)
+        _check(o, lse, q, k, v, causal, scale, f"bf16 d{d} Nq{Nq} Nk{Nk} causal={causal}")

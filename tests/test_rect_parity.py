@@ -119,6 +119,37 @@ def test_rect_sharded_long_context_sampled_rows():
     assert wo <= o_bar("f16", v) and wl <= LSE_BAR
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 256)])
+def test_rect_unaligned_start_every_dispatch_round(dtype, d):
+    # causal query rows starting at a position that is not a multiple of 32, on a grid of two dispatch
+    # rounds (B1 H16, 8192 query rows: 1024 workgroups of 128 rows at d = 128, 512 of 256 rows at
+    # d = 256), so that workgroups of both key orders run; every output finite, sampled rows of the
+    # first and last heads against the oracle
+    fa = _fa()
+    dev = torch.device("cuda")
+    B, H, Nq, a = 1, 16, 8192, 1000
+    Nk = a + Nq
+    q, k, v = _inputs(dtype, d, B, H, Nq, Nk, seed=d + 21)
+    scale = _scale(d)
+    o, lse = fa.fwd_rect(q.to(dev), k.to(dev), v.to(dev), causal=True, q_start=a, scale=scale)
+    bad = int((~torch.isfinite(o)).any(dim=-1).sum()) + int((~torch.isfinite(lse)).sum())
+    assert bad == 0, f"{bad} non-finite output rows or lse values"
+    o_np, lse_np = o.float().cpu().numpy(), lse.cpu().numpy()
+    rng = np.random.default_rng(d)
+    tile = 128 if d <= 128 else 256
+    rows = np.unique(np.concatenate([np.arange(0, Nq, tile), np.arange(31, Nq, tile), rng.integers(0, Nq, 8)]))
+    wo = wl = 0.0
+    for h in (0, H - 1):
+        kh, vh = k[0, h].double().numpy(), v[0, h].double().numpy()
+        for r in rows:
+            o_ref, lse_ref = attention_rect(q[0, h, r:r + 1], kh, vh, True, scale, q_start=a + int(r))
+            wo = max(wo, float(np.abs(o_np[0, h, r] - o_ref[0]).max()))
+            wl = max(wl, float(abs(lse_np[0, h, r] - lse_ref[0])))
+    print(f"rect {dtype} d{d} B{B} H{H} Nq{Nq} Nk{Nk} q_start{a}: max|dO| {wo:.3e} max|dlse| {wl:.3e}", flush=True)
+    assert wo <= 1e-2 and wl <= 1e-3
+    assert wo <= o_bar(dtype, v) and wl <= LSE_BAR
+
+
 def test_rect_rejects_bad_start():
     fa = _fa()
     dev = torch.device("cuda")
