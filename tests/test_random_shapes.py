@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from bars import LSE_BAR, o_bar
-from oracle import attention_ref, fp8_attention_ref, fp8_prep_ref
+from oracle import attention_rect, attention_ref, fp8_attention_ref, fp8_prep_ref
 from synth import gen_qkv, gen_signs
 
 pytestmark = pytest.mark.gpu
@@ -121,3 +121,74 @@ def test_random_shape_backward(dtype, d, B, H, N, causal, seed):
         print(f"bwd {dtype} d{d} B{B} H{H} N{N} causal={causal} {name}: max|err| {err:.3e} max|ref| {top:.3e}",
               flush=True)
         assert np.isfinite(g).all() and err <= bar * top + 1e-6
+
+
+def _cases_rect(n=16, seed=2029):
+    # queries at a random position of a longer key sequence: rectangular, key-split and decode calls
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        Nk = int(rng.integers(1, 2500 if d < 256 else 1500))
+        Nq = int(rng.integers(1, Nk + 1))
+        causal = bool(rng.integers(0, 2))
+        q_start = int(rng.integers(0, Nk - Nq + 1)) if causal else 0
+        out.append((str(rng.choice(["bf16", "f16"])), d, int(rng.integers(1, 3)), int(rng.integers(1, 3)), Nq, Nk,
+                    q_start, causal, int(rng.integers(1, 9)), 7000 + i))
+    return out
+
+
+def _check_rect(o, lse, q, k, v, causal, scale, q_start, dtype, label):
+    B, H = q.shape[:2]
+    wo = wl = 0.0
+    for b in range(B):
+        for h in range(H):
+            o_ref, lse_ref = attention_rect(q[b, h], k[b, h], v[b, h], causal, scale, q_start=q_start)
+            wo = max(wo, float(np.abs(o[b, h] - o_ref).max()))
+            wl = max(wl, float(np.abs(lse[b, h] - lse_ref).max()))
+    print(f"{label}: max|dO|={wo:.3e} max|dlse|={wl:.3e}", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), label
+    assert wo <= TOL_O and wo <= o_bar(dtype, v), label
+    assert wl <= TOL_LSE and wl <= LSE_BAR, label
+
+
+@pytest.mark.parametrize("dtype,d,B,H,Nq,Nk,q_start,causal,nsplit,seed", _cases_rect())
+def test_random_shape_rect_and_split(dtype, d, B, H, Nq, Nk, q_start, causal, nsplit, seed):
+    import exact_tiled_attention_22_amd as fa
+
+    q = gen_qkv(B, H, Nq, d, dtype, seed=seed)[0]
+    _, k, v = gen_qkv(B, H, Nk, d, dtype, seed=seed + 1)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    dev = torch.device("cuda")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    label = f"{dtype} d{d} B{B} H{H} Nq{Nq} Nk{Nk} q_start{q_start} causal={causal}"
+    o, lse = fa.fwd_rect(qd, kd, vd, causal=causal, q_start=q_start, scale=scale)
+    _check_rect(o.float().cpu().numpy(), lse.cpu().numpy(), q, k, v, causal, scale, q_start, dtype, "rect " + label)
+    o, lse = fa.fwd_split(qd, kd, vd, nsplit=nsplit, causal=causal, q_start=q_start, scale=scale)
+    _check_rect(o.float().cpu().numpy(), lse.cpu().numpy(), q, k, v, causal, scale, q_start, dtype,
+                f"split{nsplit} " + label)
+
+
+def _cases_decode(n=16, seed=2030):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        Nq = int(rng.choice([1, 1, int(rng.integers(2, 33))]))
+        Nk = int(rng.integers(Nq, 20000 if d < 256 else 8000))
+        out.append((str(rng.choice(["bf16", "f16"])), d, int(rng.integers(1, 3)), int(rng.integers(1, 5)), Nq, Nk,
+                    bool(rng.integers(0, 2)), 8000 + i))
+    return out
+
+
+@pytest.mark.parametrize("dtype,d,B,H,Nq,Nk,causal,seed", _cases_decode())
+def test_random_shape_decode(dtype, d, B, H, Nq, Nk, causal, seed):
+    import exact_tiled_attention_22_amd as fa
+
+    qf, k, v = gen_qkv(B, H, Nk, d, dtype, seed=seed)
+    q = qf[:, :, Nk - Nq:].contiguous()  # the last Nq positions
+    scale = float(np.float32(1 / math.sqrt(d)))
+    dev = torch.device("cuda")
+    o, lse = fa.fwd_decode(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale)
+    _check_rect(o.float().cpu().numpy(), lse.cpu().numpy(), q, k, v, causal, scale, Nk - Nq, dtype,
+                f"decode {dtype} d{d} B{B} H{H} Nq{Nq} Nk{Nk} causal={causal}")
