@@ -116,7 +116,11 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
  * o must overlap none of q, k, v; lse must not overlap o.  With Nq = Nk and q_start = 0 the result is
  * fa_fwd's, bit for bit.  The query rows a .. a + Nq - 1 of a sequence of Nk (q_start = a when causal)
  * give fa_fwd's rows of that range bit for bit when a is a multiple of 128 and Nq a multiple of 32 (or
- * the range ends the sequence): the kernel then puts the same rows into each wave.  Nq = 0 or B*H = 0
+ * the range ends the sequence) and, if causal, both launches walk the keys of those rows in the same
+ * order: the kernel then puts the same rows into each wave.  A causal launch with more workgroups than
+ * the GPU runs at once walks the keys of alternate dispatch rounds in
+ * opposite orders when its rows start at a multiple of 32, so rows that fall in rounds of different
+ * parity in the two launches differ by float32 summation order.  Nq = 0 or B*H = 0
  * is a no-op; Nq > 0 with Nk = 0 is FA_ERR_SHAPE.  Returns an fa_status; nothing is enqueued on error.
  */
 int fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -133,7 +137,9 @@ int fa_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse
  * over key ranges mergeable).  For shapes whose B*H*ceil(Nq/128) workgroups cannot fill the GPU, e.g.
  * one GPU's share of a sequence-sharded long-context forward.
  *   Arguments as fa_fwd_rect, plus:
- *   nsplit    : 1..64 shares per query tile (1 gives fa_fwd_rect's result bit for bit).
+ *   nsplit    : 1..64 shares per query tile (1 gives fa_fwd_rect's result bit for bit whenever
+ *               fa_fwd_rect walks every key range upward: key shares always do, fa_fwd_rect's later
+ *               dispatch rounds of a large causal grid may walk downward).
  *   workspace : DEVICE scratch of at least fa_fwd_split_workspace_bytes(B, H, Nq, d, nsplit) bytes,
  *               owned by the caller, 16-byte aligned, overlapping no tensor; contents on return are
  *               unspecified.  Calls that share a workspace must not overlap in time.
