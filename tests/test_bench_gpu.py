@@ -1,5 +1,6 @@
-"""bench.py's one JSON line, run on the GPU for a few steps of the small 16-bit workload and of the
-e4m3 workload: the fields the line promises, and a roofline time that cannot exceed the step time."""
+"""bench.py's one JSON line, run on the GPU for a few steps of the small 16-bit workload, the default
+fp16 d256 causal workload and the e4m3 workload: the fields the line promises, and a roofline time that
+cannot exceed the step time."""
 import json
 import os
 import subprocess
@@ -22,7 +23,7 @@ def _line(*args):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("config,dtype,peak", [(2, "bf16", 2500.0), (5, "fp8_e4m3", 5000.0)])
+@pytest.mark.parametrize("config,dtype,peak", [(2, "bf16", 2500.0), (4, "f16", 2500.0), (5, "fp8_e4m3", 5000.0)])
 def test_bench_line_fields_and_roofline(config, dtype, peak):
     print(f"bench.py --config {config} --steps 3 --warmup 2", flush=True)
     d = _line("--config", str(config), "--steps", "3", "--warmup", "2", "--no-cpu-baseline")
