@@ -14,6 +14,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
+ABI_VERSION = 3  # FA_ABI_VERSION of include/fa.h that these argument lists follow
 FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2, 3
 DTYPE_CODE = {
     torch.float32: FA_F32,
@@ -51,6 +52,11 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                            "(or python -m exact_tiled_attention_22_amd.build_lib)")
     L = ctypes.CDLL(LIB_PATH)
+    L.fa_abi_version.argtypes = []
+    L.fa_abi_version.restype = ctypes.c_int
+    if L.fa_abi_version() != ABI_VERSION:  # argument lists below follow this version of include/fa.h
+        raise RuntimeError(f"{LIB_PATH} implements ABI version {L.fa_abi_version()}, this binding version "
+                           f"{ABI_VERSION}: rebuild it with __graft_entry__.build()")
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     L.fa_fwd.restype = i
@@ -90,8 +96,6 @@ def lib() -> ctypes.CDLL:
     L.fa_status_str.restype = ctypes.c_char_p
     L.fa_last_error.argtypes = []
     L.fa_last_error.restype = ctypes.c_char_p
-    L.fa_abi_version.argtypes = []
-    L.fa_abi_version.restype = i
     _lib = L
     return L
 

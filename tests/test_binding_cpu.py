@@ -21,6 +21,19 @@ def test_missing_library_raises(monkeypatch, tmp_path):
         fa.split_workspace_bytes(1, 1, 8, 64, 2)
 
 
+def test_library_of_another_abi_version_is_refused(monkeypatch, tmp_path):
+    import subprocess
+
+    src = tmp_path / "fake.c"
+    src.write_text("int fa_abi_version(void) { return 99; }\n")
+    so = tmp_path / "libfa.so"
+    subprocess.run(["gcc", "-shared", "-fPIC", str(src), "-o", str(so)], check=True)
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(so))
+    with pytest.raises(RuntimeError, match="ABI version 99"):
+        binding.lib()
+
+
 @pytest.mark.parametrize("entry", ["fwd", "fwd_naive"])
 def test_host_tensors_rejected(entry):
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
