@@ -90,9 +90,9 @@ def ingest_counters(cfg_id: int, fetch_csv: str, write_csv: str) -> int:
         factor = (COPY_BYTES / 1024.0) / copy_kib
         out[counter] = {"attention_kib_per_dispatch": attn_kib, "copy_kib_per_dispatch": copy_kib,
                         "copy_scale_factor": factor, "bytes_per_launch": attn_kib * 1024.0 * factor}
-    from synth import CONFIGS
+    from synth import WORKLOADS
 
-    rec = {"config": cfg_id, "kernel_source_sha256_16": kernel_source_hash(CONFIGS[cfg_id].dtype),
+    rec = {"config": cfg_id, "kernel_source_sha256_16": kernel_source_hash(WORKLOADS[cfg_id].dtype),
            "counters": out,
            "hbm_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]}
     os.makedirs(PROFILES, exist_ok=True)
@@ -540,11 +540,11 @@ def main() -> int:
     import torch
 
     import exact_tiled_attention_22_amd as fa
-    from synth import CONFIGS, gen_fp8_workload, gen_qkv
+    from synth import WORKLOADS, gen_fp8_workload, gen_qkv
 
     if args.decode:
         return bench_decode(args)
-    w = CONFIGS[args.config]
+    w = WORKLOADS[args.config]
     if args.naive:
         return bench_naive(args, w)
     if args.shard:

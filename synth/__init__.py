@@ -5,7 +5,7 @@ attention method's arithmetic. Both sides of every parity check receive the same
 """
 
 from .gen import (  # noqa: F401
-    CONFIGS,
+    WORKLOADS,
     Workload,
     gen_fp8_workload,
     gen_qkv,

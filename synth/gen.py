@@ -60,7 +60,7 @@ class Workload:
         return f / 2.0 if self.causal else f
 
 
-CONFIGS = {
+WORKLOADS = {
     1: Workload(1, "tiny fp32 SDPA fwd B1 H1 N128 d64 non-causal", 1, 1, 128, 64, "f32", False),
     2: Workload(2, "bf16 SDPA fwd B16 H16 N1024 d128 non-causal", 16, 16, 1024, 128, "bf16", False),
     3: Workload(3, "bf16 causal SDPA fwd B2 H16 N8192 d128", 2, 16, 8192, 128, "bf16", True),
@@ -71,7 +71,7 @@ CONFIGS = {
 
 
 def workload(cfg_id: int) -> Workload:
-    return CONFIGS[cfg_id]
+    return WORKLOADS[cfg_id]
 
 
 def _rng(seed: int, stream: int, *sub: int) -> np.random.Generator:

@@ -13,7 +13,7 @@ from oracle import (
     fp8_attention_ref,
     fp8_prep_ref,
 )
-from synth import CONFIGS, gen_fp8_workload, gen_qkv, gen_signs
+from synth import WORKLOADS, gen_fp8_workload, gen_qkv, gen_signs
 
 pytestmark = pytest.mark.gpu
 
@@ -176,7 +176,7 @@ def test_fp8_zero_v_scale_block(d):
 
 def test_fp8_full_config5_sampled_rows():
     fa = _fa()
-    w = CONFIGS[5]
+    w = WORKLOADS[5]
     q, k, v, signs = gen_fp8_workload(w)
     dev = torch.device("cuda")
     q8, sq = fa.fp8_prep(q.to(dev), signs, 64)

@@ -14,7 +14,7 @@ import torch
 
 from bars import LSE_BAR, o_bar
 from oracle import attention_ref, attention_rows
-from synth import CONFIGS, gen_qkv
+from synth import WORKLOADS, gen_qkv
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +72,7 @@ def test_shape_sweep(dtype, d, N, causal):
 
 
 def test_config1_tiny_fp32_full():
-    w = CONFIGS[1]
+    w = WORKLOADS[1]
     q, k, v = gen_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=w.cfg_id)
     o, lse = _run(q, k, v, w.causal, w.scale)
     o_ref, lse_ref = attention_ref(q, k, v, w.causal, w.scale)
@@ -83,7 +83,7 @@ def test_config1_tiny_fp32_full():
 def test_full_size_configs_sampled_rows(cfg_id):
     # every head: its first and last row and one random row in each 128-row query tile, so every
     # workgroup of the launch (128 or 256 query rows of one head) has checked rows; four heads add 29
-    w = CONFIGS[cfg_id]
+    w = WORKLOADS[cfg_id]
     q, k, v = gen_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=w.cfg_id)
     o, lse = _run(q, k, v, w.causal, w.scale)
     rng = np.random.default_rng(100 + cfg_id)

@@ -3,7 +3,7 @@
 import numpy as np
 import torch
 
-from synth import CONFIGS, gen_qkv, gen_signs
+from synth import WORKLOADS, gen_qkv, gen_signs
 
 
 def test_same_seed_same_bits_and_streams_differ():
@@ -40,7 +40,7 @@ def test_outlier_count_and_factor():
 def test_signs_and_config_table():
     s = gen_signs(128, 5)
     assert s.dtype == np.int8 and set(np.unique(s)) <= {-1, 1} and len(s) == 128
-    assert [c.dtype for c in CONFIGS.values()] == ["f32", "bf16", "bf16", "f16", "fp8"]
-    assert CONFIGS[2].flops == 4.0 * 16 * 16 * 1024 * 1024 * 128
-    assert CONFIGS[3].flops == 2.0 * 2 * 16 * 8192 * 8192 * 128
-    assert CONFIGS[4].scale == 0.0625 and CONFIGS[1].scale == 0.125
+    assert [c.dtype for c in WORKLOADS.values()] == ["f32", "bf16", "bf16", "f16", "fp8"]
+    assert WORKLOADS[2].flops == 4.0 * 16 * 16 * 1024 * 1024 * 128
+    assert WORKLOADS[3].flops == 2.0 * 2 * 16 * 8192 * 8192 * 128
+    assert WORKLOADS[4].scale == 0.0625 and WORKLOADS[1].scale == 0.125
