@@ -522,7 +522,7 @@ def main() -> int:
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (dQ, dK, dV from the saved lse) instead of the forward")
     ap.add_argument("--shard", type=int, default=0, metavar="G",
-                    help="time one GPU's share of a G-way sequence-sharded causal forward (workload 3 or 4)")
+                    help="time one GPU's share of a G-way sequence-sharded causal forward (--config 3: bf16 B2 H16 N8192 d128, or --config 4: fp16 B1 H8 N16384 d256)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
