@@ -119,15 +119,16 @@ def test_rect_sharded_long_context_sampled_rows():
     assert wo <= o_bar("f16", v) and wl <= LSE_BAR
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 256)])
-def test_rect_unaligned_start_every_dispatch_round(dtype, d):
-    # causal query rows starting at a position that is not a multiple of 32, on a grid of two dispatch
-    # rounds (B1 H16, 8192 query rows: 1024 workgroups of 128 rows at d = 128, 512 of 256 rows at
-    # d = 256), so that workgroups of both key orders run; every output finite, sampled rows of the
-    # first and last heads against the oracle
+@pytest.mark.parametrize("dtype,d,a", [("bf16", 128, 1000), ("f16", 256, 1000), ("bf16", 128, 1056)])
+def test_rect_unaligned_start_every_dispatch_round(dtype, d, a):
+    # causal query rows starting at a position that is not a multiple of 32 (1000: both key orders would
+    # leave rows without a key in their first tile, so the grid walks upward), or a multiple of 32 but not
+    # of the 64-key tile (1056: odd dispatch rounds walk downward), on a grid of two dispatch rounds (B1
+    # H16, 8192 query rows: 1024 workgroups of 128 rows at d = 128, 512 of 256 rows at d = 256); every
+    # output finite, sampled rows of the first and last heads against the oracle
     fa = _fa()
     dev = torch.device("cuda")
-    B, H, Nq, a = 1, 16, 8192, 1000
+    B, H, Nq = 1, 16, 8192
     Nk = a + Nq
     q, k, v = _inputs(dtype, d, B, H, Nq, Nk, seed=d + 21)
     scale = _scale(d)
